@@ -1,0 +1,15 @@
+"""Seeded synthetic inputs shared by the CPU oracle checks and the GPU path.
+
+This package holds no attention, softmax, scatter or Burst-Gap arithmetic. It draws
+random numbers, casts them to bf16 bit patterns, and builds structured probe patterns.
+Both sides of every parity test consume the exact bytes produced here.
+"""
+
+from .inputs import (  # noqa: F401
+    WORKLOADS,
+    Workload,
+    f32_to_bf16_bits,
+    make_inputs,
+    make_placement_probe,
+    workload,
+)
