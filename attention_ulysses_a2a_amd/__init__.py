@@ -1,0 +1,178 @@
+"""MI355X-native fused attention + Ulysses post-attention all-to-all (FlashAttention-A2A).
+
+Thin Python binding over ``libxstage.so`` (C ABI in ``include/xstage.h``): argument
+marshalling only.  Tensors are torch CUDA (HIP) tensors used as plain device buffers; every
+step of the computation runs in the library's HIP kernels.  Functions carry the C names.
+
+Layouts: q, k, v, out are [B, S, H_local, D] bf16; ``out_slabs`` is either a list of P
+tensors [B, S/P, H_local, D] or one tensor [P, B, S/P, H_local, D] whose leading index
+selects the destination.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    XSTAGE_ERR_HIP,
+    XSTAGE_ERR_INVALID,
+    XSTAGE_ERR_UNSUPPORTED,
+    XSTAGE_MAX_P,
+    XSTAGE_OK,
+    BGParams,
+    LibraryMissing,
+    XStageError,
+    lib,
+    ptr_array,
+    status_name,
+)
+
+__all__ = [
+    "xstage_attn_a2a_fwd",
+    "xstage_attn_fwd",
+    "xstage_a2a_scatter",
+    "xstage_attn_a2a_unfused",
+    "xstage_burst_gap_run",
+    "xstage_wallclock_hz",
+    "xstage_bg_t_iss",
+    "xstage_status_str",
+    "LibraryMissing",
+    "XStageError",
+]
+
+
+def _check(status: int, where: str) -> None:
+    if status != XSTAGE_OK:
+        raise XStageError(status, where)
+
+
+def _dev_tensor(t, name: str):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.element_size() != 2 or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError(f"{name} must hold bf16 values (bfloat16 or 16-bit integer storage)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_of(t, stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _slab_ptrs(out_slabs):
+    import torch
+
+    if isinstance(out_slabs, torch.Tensor):
+        _dev_tensor(out_slabs, "out_slabs")
+        return [out_slabs[p].data_ptr() for p in range(out_slabs.shape[0])], out_slabs.shape[0]
+    slabs = list(out_slabs)
+    for i, s in enumerate(slabs):
+        _dev_tensor(s, f"out_slabs[{i}]")
+    return [s.data_ptr() for s in slabs], len(slabs)
+
+
+def _qkv(q, k, v):
+    _dev_tensor(q, "q"), _dev_tensor(k, "k"), _dev_tensor(v, "v")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, S, H_local, D] shape")
+    return tuple(int(x) for x in q.shape)
+
+
+def _scale(scale, D):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def xstage_attn_a2a_fwd(q, k, v, out_slabs, scale=None, stream=None) -> None:
+    """Fused attention + all-to-all scatter; see xstage_attn_a2a_fwd in include/xstage.h."""
+    import torch
+
+    B, S, H, D = _qkv(q, k, v)
+    ptrs, P = _slab_ptrs(out_slabs)
+    arr, keep = ptr_array(ptrs)
+    with torch.cuda.device(q.device):
+        st = lib().xstage_attn_a2a_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P,
+                                       _scale(scale, D), _stream_of(q, stream))
+    del keep
+    _check(st, "xstage_attn_a2a_fwd")
+
+
+def xstage_attn_fwd(q, k, v, out, scale=None, stream=None) -> None:
+    """Attention into a contiguous [B, S, H_local, D] output (first half of the serial path)."""
+    import torch
+
+    B, S, H, D = _qkv(q, k, v)
+    _dev_tensor(out, "out")
+    with torch.cuda.device(q.device):
+        st = lib().xstage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, H, D,
+                                   _scale(scale, D), _stream_of(q, stream))
+    _check(st, "xstage_attn_fwd")
+
+
+def xstage_a2a_scatter(inp, out_slabs, stream=None) -> None:
+    """Separate all-to-all send step: contiguous [B, S, H_local, D] -> P slabs."""
+    import torch
+
+    _dev_tensor(inp, "in")
+    B, S, H, D = (int(x) for x in inp.shape)
+    ptrs, P = _slab_ptrs(out_slabs)
+    arr, keep = ptr_array(ptrs)
+    with torch.cuda.device(inp.device):
+        st = lib().xstage_a2a_scatter(inp.data_ptr(), arr, B, S, H, D, P, _stream_of(inp, stream))
+    del keep
+    _check(st, "xstage_a2a_scatter")
+
+
+def xstage_attn_a2a_unfused(q, k, v, workspace, out_slabs, scale=None, stream=None) -> None:
+    """Serial baseline: attention into ``workspace`` then the separate scatter."""
+    import torch
+
+    B, S, H, D = _qkv(q, k, v)
+    _dev_tensor(workspace, "workspace")
+    ptrs, P = _slab_ptrs(out_slabs)
+    arr, keep = ptr_array(ptrs)
+    with torch.cuda.device(q.device):
+        st = lib().xstage_attn_a2a_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), workspace.data_ptr(), arr,
+                                           B, S, H, D, P, _scale(scale, D), _stream_of(q, stream))
+    del keep
+    _check(st, "xstage_attn_a2a_unfused")
+
+
+def xstage_burst_gap_run(K, V_bytes, gap_fma_iters, rounds, dst, stamps, n_dst_sets=1, nontemporal=False,
+                         stream=None) -> None:
+    """Burst-Gap store microbenchmark; ``stamps`` is an int64 device tensor of K*rounds*3 entries."""
+    import torch
+
+    if stamps.numel() < K * rounds * 3 or stamps.element_size() != 8 or not stamps.is_cuda:
+        raise ValueError("stamps must be a device tensor of K*rounds*3 64-bit entries")
+    if V_bytes and (dst is None or dst.numel() * dst.element_size() < n_dst_sets * V_bytes):
+        raise ValueError("dst must hold n_dst_sets * V_bytes bytes")
+    p = BGParams(int(K), int(rounds), int(n_dst_sets), int(bool(nontemporal)), int(V_bytes), int(gap_fma_iters),
+                 dst.data_ptr() if dst is not None else None, stamps.data_ptr())
+    with torch.cuda.device(stamps.device):
+        st = lib().xstage_burst_gap_run(ctypes.byref(p), _stream_of(stamps, stream))
+    _check(st, "xstage_burst_gap_run")
+
+
+def xstage_wallclock_hz() -> float:
+    hz = ctypes.c_double(0.0)
+    _check(lib().xstage_wallclock_hz(ctypes.byref(hz)), "xstage_wallclock_hz")
+    return hz.value
+
+
+def xstage_bg_t_iss(G_s: float, T0_s: float, V_bytes: float, R_bytes_per_s: float) -> float:
+    return lib().xstage_bg_t_iss(float(G_s), float(T0_s), float(V_bytes), float(R_bytes_per_s))
+
+
+def xstage_status_str(status: int) -> str:
+    return lib().xstage_status_str(int(status)).decode()

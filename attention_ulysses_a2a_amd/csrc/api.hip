@@ -1,0 +1,118 @@
+// extern "C" entry points of libxstage.so: argument checks, then launches.  Declarations
+// and contracts: include/xstage.h.
+#include <math.h>
+
+#include "common.hpp"
+#include "validate.hpp"
+
+namespace xstage {
+int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
+                    int P, float scale, hipStream_t stream);
+int launch_scatter(const void* in, const SlabTable& slabs, int B, int S, int H, int D, int P, hipStream_t stream);
+int launch_burst_gap(const xstage_bg_params_t& p, hipStream_t stream);
+
+static SlabTable make_table(void* const* slabs, int P) {
+  SlabTable t;
+  for (int i = 0; i < XSTAGE_MAX_P; ++i) t.p[i] = i < P ? static_cast<uint16_t*>(slabs[i]) : nullptr;
+  return t;
+}
+
+static int check_attn_slabs(const void* q, const void* k, const void* v, void* const* slabs, int B, int S, int H,
+                            int D, int P, float scale, const void* extra, unsigned long long extra_bytes) {
+  int st = check_shape(B, S, H, D, P);
+  if (st != XSTAGE_OK) return st;
+  st = check_qkv(q, k, v, scale);
+  if (st != XSTAGE_OK) return st;
+  const unsigned long long tb = tensor_bytes(B, S, H, D);
+  Range others[4] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(extra, extra_bytes)};
+  return check_slabs(slabs, P, tb / (unsigned long long)P, others, extra ? 4 : 3);
+}
+}  // namespace xstage
+
+using namespace xstage;
+
+extern "C" {
+
+int xstage_attn_a2a_fwd(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
+                        int H_local, int D, int P, float scale, void* stream) {
+  const int st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, nullptr, 0);
+  if (st != XSTAGE_OK) return st;
+  return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale,
+                         static_cast<hipStream_t>(stream));
+}
+
+int xstage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int S, int H_local, int D,
+                    float scale, void* stream) {
+  void* slabs[1] = {out};
+  const int st = check_attn_slabs(q, k, v, out ? slabs : nullptr, B, S, H_local, D, 1, scale, nullptr, 0);
+  if (st != XSTAGE_OK) return st;
+  return launch_attn_any(q, k, v, make_table(slabs, 1), B, S, H_local, D, 1, scale, static_cast<hipStream_t>(stream));
+}
+
+int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int H_local, int D, int P,
+                       void* stream) {
+  int st = check_shape(B, S, H_local, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (in == nullptr || !aligned16(in)) return XSTAGE_ERR_INVALID;
+  const unsigned long long tb = tensor_bytes(B, S, H_local, D);
+  const Range others[1] = {range_of(in, tb)};
+  st = check_slabs(out_slabs, P, tb / (unsigned long long)P, others, 1);
+  if (st != XSTAGE_OK) return st;
+  return launch_scatter(in, make_table(out_slabs, P), B, S, H_local, D, P, static_cast<hipStream_t>(stream));
+}
+
+int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* workspace, void* const* out_slabs,
+                            int B, int S, int H_local, int D, int P, float scale, void* stream) {
+  int st = check_shape(B, S, H_local, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace)) return XSTAGE_ERR_INVALID;
+  const unsigned long long tb = tensor_bytes(B, S, H_local, D);
+  const Range ws = range_of(workspace, tb);
+  if (q && (overlaps(ws, range_of(q, tb)) || overlaps(ws, range_of(k, tb)) || overlaps(ws, range_of(v, tb))))
+    return XSTAGE_ERR_INVALID;
+  st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, workspace, tb);
+  if (st != XSTAGE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* one[1] = {workspace};
+  st = launch_attn_any(q, k, v, make_table(one, 1), B, S, H_local, D, 1, scale, s);
+  if (st != XSTAGE_OK) return st;
+  return launch_scatter(workspace, make_table(out_slabs, P), B, S, H_local, D, P, s);
+}
+
+int xstage_burst_gap_run(const xstage_bg_params_t* p, void* stream) {
+  if (p == nullptr) return XSTAGE_ERR_INVALID;
+  if (p->K < 1 || p->K > 4096 || p->rounds < 1 || p->rounds > 65536 || p->n_dst_sets < 1) return XSTAGE_ERR_INVALID;
+  if (p->nontemporal != 0 && p->nontemporal != 1) return XSTAGE_ERR_INVALID;
+  if (p->stamps == nullptr || (reinterpret_cast<uintptr_t>(p->stamps) & 7u) != 0) return XSTAGE_ERR_INVALID;
+  if (p->V_bytes % (4096ull * (unsigned long long)p->K) != 0) return XSTAGE_ERR_INVALID;
+  if (p->V_bytes > 0 && (p->dst == nullptr || !aligned16(p->dst))) return XSTAGE_ERR_INVALID;
+  return launch_burst_gap(*p, static_cast<hipStream_t>(stream));
+}
+
+int xstage_wallclock_hz(double* hz) {
+  if (hz == nullptr) return XSTAGE_ERR_INVALID;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return XSTAGE_ERR_HIP;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return XSTAGE_ERR_HIP;
+  *hz = (double)khz * 1e3;
+  return XSTAGE_OK;
+}
+
+double xstage_bg_t_iss(double G_s, double T0_s, double V_bytes, double R_bytes_per_s) {
+  if (!(R_bytes_per_s > 0) || !isfinite(G_s) || !isfinite(T0_s) || !isfinite(V_bytes) || !isfinite(R_bytes_per_s))
+    return -1.0;
+  const double drain = V_bytes / R_bytes_per_s - G_s;
+  return drain > T0_s ? drain : T0_s;
+}
+
+const char* xstage_status_str(int status) {
+  switch (status) {
+    case XSTAGE_OK: return "XSTAGE_OK";
+    case XSTAGE_ERR_INVALID: return "XSTAGE_ERR_INVALID";
+    case XSTAGE_ERR_UNSUPPORTED: return "XSTAGE_ERR_UNSUPPORTED";
+    case XSTAGE_ERR_HIP: return "XSTAGE_ERR_HIP";
+    default: return "XSTAGE_UNKNOWN_STATUS";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention + Ulysses all-to-all hot path on one MI355X.
+
+A step is one call of ``xstage_attn_a2a_fwd`` on the FLUX-1024 share (B=1, S=4608,
+H_local=3, D=128, P=8 destination slabs of [576, 3, 128]): non-causal attention over the full
+sequence with the post-attention all-to-all written from the epilogue.  Inputs are seeded
+synthetic bf16 tensors resident in HBM before the timed region.  Prints one JSON line.
+
+Extra legs (reported inside the same line): the serial path (attention into a contiguous
+buffer, then the separate scatter kernel), attention alone (P=1), and the CPU oracle timed
+on a bounded sample of the same workload (``cpu_baseline``).  ``--bg`` instead runs the
+Burst-Gap store sweep and prints one JSON line per point plus the fitted parameters.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused attn+A2A-scatter TFLOP/s & % bf16 MFMA peak (S=4608, 1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_a2a_flux1024.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "attention_ulysses_a2a_amd", "csrc", f)
+                  for f in ("attn_a2a.hip", "common.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="flux1024", help="synth workload name (tiny, flux1024, flux2048, video)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--bg", action="store_true", help="run the Burst-Gap store sweep instead")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, torch):
+    """Average ms per call over `steps` back-to-back calls on the current stream (HIP events)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, qb, kb, vb, seconds):
+    """Times the oracle (as it stands) on whole query-row blocks of the workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    q, k, v = (oracle.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    rows_done = 0
+    t0 = time.perf_counter()
+    rng_rows = np.arange(w.S)
+    block = 512
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        sel = rng_rows[(i * block) % w.S:(i * block) % w.S + block]
+        oracle.attention_fp64(q, k, v, w.scale, rows=sel)
+        rows_done += len(sel)
+        i += 1
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.B * rows_done * w.S * w.D * w.H
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows_done} query rows x all {w.H} heads (blocks of {block}) of the {w.name} workload over the "
+                  f"full key set, float64 numpy, {dt:.1f} s",
+        "seconds": dt,
+    }
+
+
+def traffic_entry(achieved_bytes_per_launch=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it is current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def bench_attention(args, torch, xs):
+    import numpy as np
+
+    from synth import make_inputs, workload
+
+    w = workload(args.workload)
+    qb, kb, vb = make_inputs(w)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    slabs = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((w.B, w.S, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    out1 = torch.empty((w.B, w.S, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    slab_list = [slabs[p] for p in range(w.P)]
+
+    fused = lambda: xs.xstage_attn_a2a_fwd(q, k, v, slab_list, w.scale)  # noqa: E731
+    unfused = lambda: xs.xstage_attn_a2a_unfused(q, k, v, ws, slab_list, w.scale)  # noqa: E731
+    attn_only = lambda: xs.xstage_attn_fwd(q, k, v, out1, w.scale)  # noqa: E731
+    scatter_only = lambda: xs.xstage_a2a_scatter(ws, slab_list)  # noqa: E731
+
+    # the timed region: exactly `steps` fused steps bracketed by synchronizations
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        fused()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+
+    # comparison legs (outside the timed region)
+    ms_unfused = timed(unfused, args.steps, args.warmup, torch)
+    ms_attn = timed(attn_only, args.steps, args.warmup, torch)
+    ms_scatter = timed(scatter_only, args.steps, args.warmup, torch)
+
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, K x 0.5; inputs resident in HBM)",
+        "config": {
+            "workload": f"{w.name} share: B={w.B} S={w.S} H_local={w.H} D={w.D} P={w.P} slabs [{w.S // w.P},{w.H},{w.D}]",
+            "global_batch": w.B,
+            "seq_len": w.S,
+            "parallelism": f"one GPU's Ulysses share (P={w.P} destination slabs in local HBM)",
+        },
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fused_vs_unfused": round(ms_unfused / ms, 4),
+        "fused_vs_attention_only": round(ms / ms_attn, 4),
+        "ms_unfused": ms_unfused,
+        "ms_attention_only": ms_attn,
+        "ms_scatter_only": ms_scatter,
+        "scatter_GBps": round(2 * w.out_bytes / (ms_scatter * 1e-3) / 1e9, 1),
+        "wall_s_timed_region": t_wall,
+    }
+    hbm = traffic_entry()
+    res["roofline"] = {
+        "bound": "mfma",
+        "achieved": round(tflops, 3),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": hbm,
+    }
+    return w, (qb, kb, vb), res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the P Ulysses destinations are local "
+                                   "receive buffers; no collective or multi-GPU path exists (use --gpus 1)"}))
+        sys.exit(2)
+    import torch
+
+    import attention_ulysses_a2a_amd as xs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    xs.lib()  # fail loudly if the HIP library is missing
+    if args.bg:
+        from attention_ulysses_a2a_amd.bg_sweep import run_sweep
+
+        run_sweep(torch, xs)
+        return
+    w, inputs, res = bench_attention(args, torch, xs)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, *inputs, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,127 @@
+/*
+ * xstage.h - C ABI of libxstage.so: one GPU's share of Ulysses sequence-parallel attention
+ * with the post-attention all-to-all fused into the attention epilogue, for MI355X (gfx950).
+ *
+ * Source of the method: the four-language gist.science explainer of arXiv 2607.23264,
+ * "X-Stage: An Overlooked Pipeline Stage for Communication-Computation Overlap in DiT
+ * Inference", technical summary.
+ *   - "Contributions", FlashAttention-A2A (piggybacking) item: for Ulysses-style sequence
+ *     parallel attention the post-attention all-to-all is fused into FlashAttention; the
+ *     owner of each output tile issues its stores toward the destinations and immediately
+ *     goes on with the next tile's query loop, with no dedicated communication wave.
+ *   - "Results", FlashAttention-A2A: the fused kernel is compared with serial execution
+ *     (attention, then a separate all-to-all).
+ *   - "Methodology": the Burst-Gap model T_iss(G;K,V) = max(T0_iss(K,V), V/R - G) and the
+ *     quantities T0_iss, R, Q; "Contributions", characterisation item: they are measured
+ *     with parameterised store microbenchmarks.
+ *
+ * On one GPU the P destinations are P receive buffers ("slabs") in local HBM standing in
+ * for the peers' receive buffers.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are bf16 bit patterns (uint16 storage), row-major, last index fastest, on the
+ *     current HIP device.  Every tensor pointer must be 16-byte aligned.
+ *   - q, k, v and the contiguous attention output are [B, S, H_local, D] ("BSHD").
+ *   - Slab p (0 <= p < P) is [B, S/P, H_local, D] and receives sequence rows
+ *     [p*S/P, (p+1)*S/P): slab[p][b][r][h][d] = O[b][p*S/P + r][h][d].
+ *   - `out_slabs` is a HOST array of P device pointers; the pointers are copied by value
+ *     into the kernel arguments, so the array may be freed as soon as the call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work and return;
+ *     they never synchronize.  Except where stated, they never allocate or free memory.
+ *   - Errors: every argument check runs before any HIP call; on an error nothing is
+ *     launched and no output byte is touched.  Faults inside kernels surface at the
+ *     caller's next synchronization.  XSTAGE_ERR_HIP reports the HIP launch status.
+ *   - Attention: O = softmax(scale * Q K^T) V per (b, h), non-causal, products and sums in
+ *     fp32, output rounded to bf16 (round to nearest, ties to even).  scale may be any
+ *     finite value, including 0 and negative values.
+ *   - Thread safety: entry points hold no mutable state and may be called concurrently.
+ */
+#ifndef XSTAGE_H_
+#define XSTAGE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define XSTAGE_MAX_P 64
+
+typedef enum {
+  XSTAGE_OK = 0,
+  XSTAGE_ERR_INVALID = 1,     /* null pointer, size <= 0, S % P != 0, misaligned pointer,
+                                 non-finite scale, overlapping buffers, bad parameters */
+  XSTAGE_ERR_UNSUPPORTED = 2, /* D not in {64, 128}, P > XSTAGE_MAX_P, a tensor of
+                                 2^31 elements or more */
+  XSTAGE_ERR_HIP = 3          /* the HIP runtime refused the launch */
+} xstage_status_t;
+
+/* Fused attention + post-attention all-to-all scatter ("Contributions", FlashAttention-A2A
+ * piggybacking item).  q, k, v: [B, S, H_local, D]; out_slabs: P device pointers, each to
+ * [B, S/P, H_local, D].  Each output tile is written straight from the attention epilogue
+ * into the slab that owns its rows; the issuing wave does not wait for the stores and
+ * goes on with its next tile.  Slabs must not overlap each other or q, k, v. */
+int xstage_attn_a2a_fwd(const void* q, const void* k, const void* v, void* const* out_slabs,
+                        int B, int S, int H_local, int D, int P, float scale, void* stream);
+
+/* Attention alone into a contiguous [B, S, H_local, D] output (the first half of the serial
+ * baseline of "Results", FlashAttention-A2A).  `out` must not overlap q, k, v. */
+int xstage_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                    int B, int S, int H_local, int D, float scale, void* stream);
+
+/* The separate all-to-all send step of the serial baseline: copies a contiguous
+ * [B, S, H_local, D] tensor into the P slabs.  Slabs must not overlap `in` or each other. */
+int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int H_local,
+                       int D, int P, void* stream);
+
+/* Serial baseline: xstage_attn_fwd into `workspace` ([B, S, H_local, D], caller-owned),
+ * then xstage_a2a_scatter into the slabs, both on `stream`.  Same result as
+ * xstage_attn_a2a_fwd, bit for bit. */
+int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* workspace,
+                            void* const* out_slabs, int B, int S, int H_local, int D, int P,
+                            float scale, void* stream);
+
+/* Burst-Gap store microbenchmark ("Methodology"; "Contributions", characterisation item).
+ * K producer workgroups (256 threads each) run `rounds` rounds of: a burst that stores
+ * V_bytes / K bytes as 16-byte stores into the producer's share of destination set
+ * (round % n_dst_sets), then a dependent FMA loop of `gap_fma_iters` iterations (the gap G).
+ * No wait for store completion inside a round; after the last round's gap the producer
+ * waits for all its stores to complete.
+ *   dst:    device buffer of at least n_dst_sets * V_bytes bytes (caller guarantees size).
+ *   stamps: device uint64 [K][rounds][3] in wall-clock ticks (xstage_wallclock_hz):
+ *           [0] burst start (all waves of the producer at the start barrier),
+ *           [1] last store of the burst issued by every wave (no wait for completion),
+ *           [2] end of the gap; in the last round, taken after the wait for completion.
+ *   V_bytes must be a multiple of K * 4096 (each producer stores whole 4 KiB rows of
+ *   16-byte lanes); V_bytes = 0 runs the gap alone (calibration).  1 <= K <= 4096,
+ *   1 <= rounds <= 65536, n_dst_sets >= 1, nontemporal in {0, 1}. */
+typedef struct {
+  int K;
+  int rounds;
+  int n_dst_sets;
+  int nontemporal;
+  unsigned long long V_bytes;
+  unsigned int gap_fma_iters;
+  void* dst;
+  unsigned long long* stamps;
+} xstage_bg_params_t;
+
+int xstage_burst_gap_run(const xstage_bg_params_t* p, void* stream);
+
+/* Frequency of the device wall clock used by the microbenchmark stamps, in Hz
+ * (hipDeviceAttributeWallClockRate of the current device).  The only entry point that
+ * queries the device. */
+int xstage_wallclock_hz(double* hz);
+
+/* Burst-Gap issue time in seconds ("Methodology"): max(T0, V/R - G), with V in bytes and R
+ * in bytes per second.  Returns a negative value for R <= 0 or non-finite inputs. */
+double xstage_bg_t_iss(double G_s, double T0_s, double V_bytes, double R_bytes_per_s);
+
+/* Static string naming a status code. */
+const char* xstage_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XSTAGE_H_ */

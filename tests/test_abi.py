@@ -1,0 +1,193 @@
+"""The C ABI: exported symbols match include/xstage.h; every invalid argument is rejected
+with its status before anything is launched; the host-side Burst-Gap helper matches the
+hand-evaluated values.  Runs without a GPU (no call here reaches a kernel launch)."""
+
+import json
+import math
+import os
+import re
+
+import pytest
+
+import attention_ulysses_a2a_amd as xs
+from attention_ulysses_a2a_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED = _lib.XSTAGE_ERR_INVALID, _lib.XSTAGE_ERR_UNSUPPORTED
+
+
+def _gpu_visible():
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# The error-path cases below pass fake (never dereferenced) device addresses.  They are run
+# only where no device is visible, so that a missing check could never reach a launch.
+no_device = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer error paths run only without a visible device")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from attention_ulysses_a2a_amd.build import build
+
+        build()
+    return _lib.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "xstage.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|double|const char\*)\s+(xstage_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_library_agree(L):
+    names = header_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_status_strings(L):
+    assert xs.xstage_status_str(0) == "XSTAGE_OK"
+    assert xs.xstage_status_str(1) == "XSTAGE_ERR_INVALID"
+    assert xs.xstage_status_str(2) == "XSTAGE_ERR_UNSUPPORTED"
+    assert xs.xstage_status_str(3) == "XSTAGE_ERR_HIP"
+    assert xs.xstage_status_str(99) == "XSTAGE_UNKNOWN_STATUS"
+
+
+def test_bg_t_iss_hand_values(L):
+    with open(os.path.join(ROOT, "tests", "golden", "burst_gap_hand_values.json")) as f:
+        g = json.load(f)
+    for c in g["page_formula"]:
+        got = xs.xstage_bg_t_iss(c["G_s"], g["T0_s"], g["V_bytes"], g["R_bytes_per_s"])
+        assert abs(got - c["T_iss_s"]) <= g["tolerance_s"]
+    assert xs.xstage_bg_t_iss(0, 1e-6, 1e6, 0.0) < 0
+    assert xs.xstage_bg_t_iss(float("nan"), 1e-6, 1e6, 1e9) < 0
+
+
+# ---- error paths with fake addresses ------------------------------------------------------
+Q, K, V = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000
+SLAB0 = 0x40_0000_0000
+GAP = 0x1_0000_0000
+
+
+def slabs(P, base=SLAB0, step=GAP):
+    return [base + p * step for p in range(P)]
+
+
+def fwd(L, q=Q, k=K, v=V, sl=None, B=1, S=256, H=2, D=64, P=2, scale=0.125):
+    sl = slabs(P) if sl is None else sl
+    arr, keep = _lib.ptr_array(sl)
+    return L.xstage_attn_a2a_fwd(q, k, v, arr if sl != "null" else None, B, S, H, D, P, scale, None)
+
+
+@no_device
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(v=0), INVALID),
+    (dict(B=0), INVALID), (dict(S=-1), INVALID), (dict(H=0), INVALID), (dict(P=0), INVALID), (dict(D=0), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(D=256), UNSUPPORTED),
+    (dict(S=65 * 64, P=65), UNSUPPORTED),
+    (dict(S=1001, P=8), INVALID),
+    (dict(q=Q + 8), INVALID), (dict(v=V + 2), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(S=1 << 20, H=16, D=128, P=1), UNSUPPORTED),
+])
+def test_fused_rejects(L, kw, code):
+    assert fwd(L, **kw) == code
+
+
+@no_device
+def test_fused_rejects_bad_slabs(L):
+    assert L.xstage_attn_a2a_fwd(Q, K, V, None, 1, 256, 2, 64, 2, 0.125, None) == INVALID
+    assert fwd(L, sl=[SLAB0, 0]) == INVALID                       # null slab
+    assert fwd(L, sl=[SLAB0, SLAB0 + 16]) == INVALID              # slabs overlap
+    assert fwd(L, sl=[SLAB0, Q + 64]) == INVALID                  # slab inside q
+    assert fwd(L, sl=[SLAB0, V - 16]) == INVALID                  # slab runs into v
+    assert fwd(L, sl=[SLAB0, SLAB0 + GAP + 4]) == INVALID         # misaligned slab
+    # adjacent but disjoint slabs are fine up to the launch: only check they pass the
+    # overlap rule by making another argument invalid afterwards
+    slab_bytes = 1 * 128 * 2 * 64 * 2
+    assert fwd(L, sl=[SLAB0, SLAB0 + slab_bytes], scale=float("nan")) == INVALID
+
+
+@no_device
+def test_attn_fwd_rejects(L):
+    f = L.xstage_attn_fwd
+    assert f(Q, K, V, 0, 1, 256, 2, 64, 0.125, None) == INVALID
+    assert f(Q, K, V, K + 32, 1, 256, 2, 64, 0.125, None) == INVALID   # out overlaps k
+    assert f(Q, K, V, SLAB0 + 8, 1, 256, 2, 64, 0.125, None) == INVALID
+    assert f(Q, K, V, SLAB0, 1, 256, 2, 80, 0.125, None) == UNSUPPORTED
+    assert f(Q, K, V, SLAB0, 1, 0, 2, 64, 0.125, None) == INVALID
+
+
+@no_device
+def test_scatter_rejects(L):
+    arr, keep = _lib.ptr_array(slabs(2))
+    f = L.xstage_a2a_scatter
+    assert f(0, arr, 1, 256, 2, 64, 2, None) == INVALID
+    assert f(Q + 4, arr, 1, 256, 2, 64, 2, None) == INVALID
+    assert f(Q, None, 1, 256, 2, 64, 2, None) == INVALID
+    assert f(Q, arr, 1, 255, 2, 64, 2, None) == INVALID
+    bad, keep2 = _lib.ptr_array([SLAB0, Q + 128])
+    assert f(Q, bad, 1, 256, 2, 64, 2, None) == INVALID
+    assert f(Q, arr, 1, 256, 2, 48, 2, None) == UNSUPPORTED
+
+
+@no_device
+def test_unfused_rejects(L):
+    arr, keep = _lib.ptr_array(slabs(2))
+    f = L.xstage_attn_a2a_unfused
+    W = 0x50_0000_0000
+    assert f(Q, K, V, 0, arr, 1, 256, 2, 64, 2, 0.125, None) == INVALID
+    assert f(Q, K, V, W + 8, arr, 1, 256, 2, 64, 2, 0.125, None) == INVALID
+    assert f(Q, K, V, Q + 256, arr, 1, 256, 2, 64, 2, 0.125, None) == INVALID   # workspace overlaps q
+    assert f(Q, K, V, SLAB0 + GAP - 64, arr, 1, 256, 2, 64, 2, 0.125, None) == INVALID  # overlaps slab 1
+    assert f(Q, K, V, W, arr, 1, 256, 2, 64, 2, float("nan"), None) == INVALID
+    assert f(Q, K, V, W, arr, 1, 256, 2, 64, 3, 0.125, None) == INVALID
+
+
+@no_device
+def test_burst_gap_rejects(L):
+    import ctypes
+
+    def run(**kw):
+        base = dict(K=64, rounds=8, n_dst_sets=1, nontemporal=0, V_bytes=1 << 20, gap_fma_iters=10,
+                    dst=SLAB0, stamps=Q)
+        base.update(kw)
+        p = _lib.BGParams(**base)
+        return L.xstage_burst_gap_run(ctypes.byref(p), None)
+
+    assert L.xstage_burst_gap_run(None, None) == INVALID
+    assert run(K=0) == INVALID
+    assert run(K=5000) == INVALID
+    assert run(rounds=0) == INVALID
+    assert run(n_dst_sets=0) == INVALID
+    assert run(nontemporal=2) == INVALID
+    assert run(stamps=0) == INVALID
+    assert run(stamps=Q + 4) == INVALID
+    assert run(V_bytes=(1 << 20) + 4096) == INVALID   # not a multiple of K * 4096
+    assert run(dst=0) == INVALID
+    assert run(dst=SLAB0 + 8) == INVALID
+
+
+@no_device
+def test_wallclock_rejects_null(L):
+    assert L.xstage_wallclock_hz(None) == INVALID
+
+
+def test_xcd_unit_order_is_a_bijection():
+    """Host replica of the kernel's workgroup -> unit remap (XCD i % 8 gets a contiguous range)."""
+    for n in list(range(1, 70)) + [108, 216, 396, 1280, 1281, 2565]:
+        q8, r8 = n >> 3, n & 7
+        seen = set()
+        for i in range(n):
+            xcd, slot = i & 7, i >> 3
+            L = xcd * (q8 + 1) + slot if xcd < r8 else r8 * (q8 + 1) + (xcd - r8) * q8 + slot
+            assert 0 <= L < n
+            seen.add(L)
+        assert len(seen) == n
