@@ -25,6 +25,7 @@
 
 #include "common.hpp"
 #include "validate.hpp"
+#include "workspace.hpp"
 
 namespace xstage {
 
@@ -61,9 +62,13 @@ struct AttnArgs {
   SlabTable slabs;
   int B, S, H, S_P;
   int n_mtiles;
-  int n_units;
-  float c;         // |scale| * log2(e): scores are turned into base-2 logits
-  uint32_t qflip;  // 0x80008000 for a negative scale: Q is negated on load
+  int n_units;       // workgroups: (b, h, m-tile) tiles x key splits
+  int n_split;       // key-range splits per tile (1: no merge)
+  int kvb_per_split; // 64-key blocks per split
+  float c;           // |scale| * log2(e): scores are turned into base-2 logits
+  uint32_t qflip;    // 0x80008000 for a negative scale: Q is negated on load
+  f32x4* partial;    // split partials: [tile][split][wave][PREC chunks][64 lanes] (n_split > 1)
+  uint32_t* counters;  // per-tile arrival counters, zero between launches (n_split > 1)
 };
 
 // A pointer read through a wave-uniform index, kept in scalar registers.
@@ -96,8 +101,10 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     const int q8 = n >> 3, r8 = n & 7, xcd = i & 7, slot = i >> 3;
     L = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
   }
-  const int mt = L % a.n_mtiles;
-  const int bh = L / a.n_mtiles;
+  const int tile = L / a.n_split;
+  const int split = L - tile * a.n_split;
+  const int mt = tile % a.n_mtiles;
+  const int bh = tile / a.n_mtiles;
   const int h = bh % a.H;
   const int b = bh / a.H;
   const int m0 = mt * C::BM;
@@ -121,22 +128,19 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     }
   }
 
-  // Global -> register -> LDS staging of one K/V block (16-byte chunks, rows beyond S zeroed).
+  // Global -> register -> LDS staging of one K/V block (16-byte chunks).
   u32x4 kr[C::NLD], vr[C::NLD];
+  // Keys past the end are clamped to row S-1: their scores are masked and their weights
+  // set to exactly zero, so the duplicated (finite) rows contribute nothing.  No branches.
   auto gload = [&](int n0) {
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i) {
       const int lin = i * C::THREADS + tid;
       const int row = lin / C::CH, ch = lin % C::CH;
-      const int key = n0 + row;
-      if (key < S) {
-        const uint32_t off = (uint32_t)key * rs + ch * 8;
-        kr[i] = *reinterpret_cast<const u32x4*>(kb + off);
-        vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
-      } else {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int key = min(n0 + row, S - 1);
+      const uint32_t off = (uint32_t)key * rs + ch * 8;
+      kr[i] = *reinterpret_cast<const u32x4*>(kb + off);
+      vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
     }
   };
   auto lstore = [&](char* kbuf, char* vbuf) {
@@ -169,14 +173,16 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   const float c = a.c;
 
   const int nkv = (S + C::BN - 1) / C::BN;
-  gload(0);
+  const int j0 = split * a.kvb_per_split;
+  const int j1 = min(j0 + a.kvb_per_split, nkv);
+  gload(j0 * C::BN);
   lstore(smem, smem + C::BLKB);
   __syncthreads();
 
-  for (int j = 0; j < nkv; ++j) {
-    const char* kbuf = smem + (j & 1) * 2 * C::BLKB;
+  for (int j = j0; j < j1; ++j) {
+    const char* kbuf = smem + ((j - j0) & 1) * 2 * C::BLKB;
     const char* vbuf = kbuf + C::BLKB;
-    const bool more = j + 1 < nkv;
+    const bool more = j + 1 < j1;
     if (more) gload((j + 1) * C::BN);
 
     // S^T (keys x queries) for two 32-key tiles
@@ -258,10 +264,66 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     }
 
     if (more) {
-      char* nk = smem + ((j + 1) & 1) * 2 * C::BLKB;
+      char* nk = smem + ((j + 1 - j0) & 1) * 2 * C::BLKB;
       lstore(nk, nk + C::BLKB);
     }
     __syncthreads();
+  }
+
+  // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
+  // merges them (exact rescaling by exp2(m_s - m)) and runs the epilogue for the tile.
+  if (a.n_split > 1) {
+    __shared__ int last_flag;
+    constexpr int PREC = 4 * C::DT + 1;  // 16-byte chunks per lane: O registers, then (m, l)
+    auto rec = [&](int sp) { return a.partial + ((size_t)(tile * a.n_split + sp) * 4 + w) * PREC * 64 + lane; };
+    {
+      f32x4* r = rec(split);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          r[(dt * 4 + q4) * 64] = f32x4{o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
+      r[(PREC - 1) * 64] = f32x4{m_run, l_run, 0.f, 0.f};
+    }
+    // Each wave's stores complete (workgroup-scope release), then ONE device-scope release
+    // for the whole workgroup before its arrival is counted: a device-scope fence writes
+    // back the XCD's L2, which is far too costly to repeat per wave.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t prev = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int is_last = prev == (uint32_t)(a.n_split - 1);
+      if (is_last) {
+        __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other splits' partials
+      }
+      last_flag = is_last;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    // Merge in split order from memory (own partial included), so the result does not
+    // depend on which split arrived last.
+    float m_all = -INFINITY;
+    for (int sp = 0; sp < a.n_split; ++sp) m_all = __builtin_fmaxf(m_all, rec(sp)[(PREC - 1) * 64][0]);
+    l_run = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x16{};
+    for (int sp = 0; sp < a.n_split; ++sp) {
+      const f32x4* r = rec(sp);
+      const f32x4 ml = r[(PREC - 1) * 64];
+      const float f = __builtin_amdgcn_exp2f(ml[0] - m_all);
+      l_run += ml[1] * f;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 x = r[(dt * 4 + q4) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[dt][4 * q4 + e] += x[e] * f;
+        }
+    }
+    m_run = m_all;
   }
 
   // ---- epilogue: normalise, bf16, restage per wave, store rows into their slabs ----------
@@ -336,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
 
 template <int D>
 static int launch_attn(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H,
-                       int P, float scale, hipStream_t stream) {
+                       int P, float scale, const SplitPlan& plan, hipStream_t stream) {
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -347,17 +409,32 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.H = H;
   a.S_P = S / P;
   a.n_mtiles = (S + AttnCfg<D>::BM - 1) / AttnCfg<D>::BM;
-  a.n_units = B * H * a.n_mtiles;
+  a.n_split = plan.n_split;
+  a.kvb_per_split = plan.kvb_per_split;
+  a.n_units = B * H * a.n_mtiles * plan.n_split;
   a.c = fabsf(scale) * kLog2e;
   a.qflip = std::signbit(scale) ? 0x80008000u : 0u;
+  a.partial = static_cast<f32x4*>(plan.partial);
+  a.counters = plan.counters;
   hipLaunchKernelGGL(attn_a2a_kernel<D>, dim3(a.n_units), dim3(AttnCfg<D>::THREADS), 0, stream, a);
   return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
 }
 
+// Bytes of split partials for one tile and one split (4 waves x PREC chunks x 64 lanes x 16 B).
+static size_t partial_bytes_per_unit(int D) { return (size_t)4 * (4 * (D / 32) + 1) * 64 * 16; }
+
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
                     int P, float scale, hipStream_t stream) {
-  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, stream);
-  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, stream);
+  const int n_tiles = B * H * ((S + 127) / 128);
+  const int nkv = (S + 63) / 64;
+  SplitPlan plan = choose_split(n_tiles, nkv, partial_bytes_per_unit(D));
+  if (plan.n_split > 1) {
+    const int st = acquire_workspace(stream, (size_t)n_tiles * plan.n_split * partial_bytes_per_unit(D), n_tiles,
+                                     &plan.partial, &plan.counters);
+    if (st != XSTAGE_OK) return st;
+  }
+  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, stream);
+  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, stream);
 }
 
 }  // namespace xstage
