@@ -128,29 +128,27 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     }
   }
 
-  // Global -> register -> LDS staging of one K/V block (16-byte chunks).
-  u32x4 kr[C::NLD], vr[C::NLD];
-  // Keys past the end are clamped to row S-1: their scores are masked and their weights
-  // set to exactly zero, so the duplicated (finite) rows contribute nothing.  No branches.
-  auto gload = [&](int n0) {
+  // K/V blocks go from global memory straight into LDS (global_load_lds_dwordx4: no
+  // registers).  One instruction of wave w fills the 1 KiB LDS segment (i*4 + w) of a
+  // block, lane by lane, so each lane fetches the global chunk that belongs at its LDS slot
+  // under the swizzle.  Keys past the end are clamped to row S-1: their scores are masked
+  // and their weights set to exactly zero, so the duplicated (finite) rows add nothing.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t ld_off[C::NLD];  // element offset of this lane's chunk within a key block
+  int ld_row[C::NLD];
+#pragma unroll
+  for (int i = 0; i < C::NLD; ++i) {
+    const int P = (i * 4 + w) * 64 + lane;
+    const int row = P / C::CH, pc = P % C::CH;
+    ld_row[i] = row;
+    ld_off[i] = (uint32_t)((pc ^ swz<D>(row)) * 8);
+  }
+  auto dload = [&](const uint16_t* src, char* dst, int n0) {
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i) {
-      const int lin = i * C::THREADS + tid;
-      const int row = lin / C::CH, ch = lin % C::CH;
-      const int key = min(n0 + row, S - 1);
-      const uint32_t off = (uint32_t)key * rs + ch * 8;
-      kr[i] = *reinterpret_cast<const u32x4*>(kb + off);
-      vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
-    }
-  };
-  auto lstore = [&](char* kbuf, char* vbuf) {
-#pragma unroll
-    for (int i = 0; i < C::NLD; ++i) {
-      const int lin = i * C::THREADS + tid;
-      const int row = lin / C::CH, ch = lin % C::CH;
-      const int off = row * C::ROWB + ((ch ^ swz<D>(row)) << 4);
-      *reinterpret_cast<u32x4*>(kbuf + off) = kr[i];
-      *reinterpret_cast<u32x4*>(vbuf + off) = vr[i];
+      const int key = min(n0 + ld_row[i], S - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(src + (uint32_t)key * rs + ld_off[i]),
+                                       (__attribute__((address_space(3))) void*)(dst + (i * 4 + wu) * 1024), 16, 0, 0);
     }
   };
 
@@ -172,86 +170,89 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   float l_run = 0.f;
   const float c = a.c;
 
-  const int nkv = (S + C::BN - 1) / C::BN;
-  const int j0 = split * a.kvb_per_split;
-  const int j1 = min(j0 + a.kvb_per_split, nkv);
-  gload(j0 * C::BN);
-  lstore(smem, smem + C::BLKB);
-  __syncthreads();
-
-  for (int j = j0; j < j1; ++j) {
-    const char* kbuf = smem + ((j - j0) & 1) * 2 * C::BLKB;
-    const char* vbuf = kbuf + C::BLKB;
-    const bool more = j + 1 < j1;
-    if (more) gload((j + 1) * C::BN);
-
-    // S^T (keys x queries) for two 32-key tiles
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  // S^T = K Q^T for one 64-key block held in LDS (two 32-key tiles)
+  auto qk = [&](const char* kbuf, f32x16* st) {
+    st[0] = f32x16{};
+    st[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const char* p = kbuf + (t * 32 + krow) * C::ROWB + (((2 * ks + hl) ^ kswz) << 4);
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(p);
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[t], 0, 0, 0);
       }
     }
+  };
 
-    // keys beyond S in the last block: excluded from the max here, weight forced to zero below
-    const int n0 = j * C::BN;
-    const bool tail = n0 + C::BN > S;
+  // Online softmax, base 2 with the scale folded into c, split in two steps so that the
+  // exponentials of block j can share one basic block with the score MFMAs of block j+1:
+  //  * rescale(): block max; the running max is only raised when the block exceeds it by
+  //    more than kLazy (log2 units), so weights stay below 2^kLazy (exact after the final
+  //    division) and the O rescale, one multiply per accumulator, is skipped for most blocks;
+  //  * exp_pack(): weights, row sums, and bf16 packing into the B operand of the PV MFMA.
+  // Keys past S exist only in the very last block (`tail`): masked out of the max, weight 0.
+  constexpr float kLazy = 8.0f;
+  const int nkv = (S + C::BN - 1) / C::BN;
+  auto key_of = [&](int n0, int t, int r) { return n0 + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3); };
+  auto rescale = [&](f32x16* st, int n0, bool tail) {
     if (tail) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= S) s[t][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (key_of(n0, t, r) >= S) st[t][r] = -INFINITY;
     }
-
-    // online softmax in base 2 (exp(x) = exp2(x * log2 e); scale folded into c)
-    float mx = s[0][0];
+    float m4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& x = st[q >> 1];
+      const int r0 = (q & 1) * 8;
+      const float u = __builtin_fmaxf(__builtin_fmaxf(x[r0], x[r0 + 1]), __builtin_fmaxf(x[r0 + 2], x[r0 + 3]));
+      const float v = __builtin_fmaxf(__builtin_fmaxf(x[r0 + 4], x[r0 + 5]), __builtin_fmaxf(x[r0 + 6], x[r0 + 7]));
+      m4[q] = __builtin_fmaxf(u, v);
+    }
+    const float mx = max_with_partner32(__builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3]))) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+  };
+  auto exp_pack = [&](f32x16* st, bf16x8* pb, int n0, bool tail) {
+    const float neg_m = -m_run;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[t][r]);
-    mx = max_with_partner32(mx);
-    const float m_new = __builtin_fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float neg_m = -m_new;
-    float rsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, neg_m));
+      for (int r = 0; r < 16; ++r) st[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][r], c, neg_m));
     if (tail) {  // (-inf) * c is NaN when scale == 0: zero the masked weights explicitly
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= S) s[t][r] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (key_of(n0, t, r) >= S) st[t][r] = 0.f;
     }
+    float rs4[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rsum += s[t][r];
-    l_run = l_run * alpha + rsum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& x = st[q >> 1];
+      const int r0 = (q & 1) * 8;
+      rs4[q] = ((x[r0] + x[r0 + 1]) + (x[r0 + 2] + x[r0 + 3])) + ((x[r0 + 4] + x[r0 + 5]) + (x[r0 + 6] + x[r0 + 7]));
+      const u32x4 pk = {pack_bf16x2(x[r0 + 0], x[r0 + 1]), pack_bf16x2(x[r0 + 2], x[r0 + 3]),
+                        pack_bf16x2(x[r0 + 4], x[r0 + 5]), pack_bf16x2(x[r0 + 6], x[r0 + 7])};
+      pb[q] = __builtin_bit_cast(bf16x8, pk);
+    }
+    l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+  };
 
-    // O^T += V^T P^T, four 16-key steps; k-step t uses registers 8*(t&1)..+7 of s[t>>1],
-    // i.e. keys 16t + 8*(jj/4) + 4*hl + jj%4 for slot jj.
+  // O^T += V^T P^T, four 16-key steps; k-step t uses pb[t] = registers 8*(t&1)..+7 of the
+  // score tile t>>1, i.e. keys 16t + 8*(jj/4) + 4*hl + jj%4 for slot jj.
+  auto pv = [&](const char* vbuf, const bf16x8* pb) {
 #pragma unroll
     for (int t = 0; t < C::BN / 16; ++t) {
-      const f32x16& st = s[t >> 1];
-      const int rb = 8 * (t & 1);
-      const u32x4 pk = {pack_bf16x2(st[rb + 0], st[rb + 1]), pack_bf16x2(st[rb + 2], st[rb + 3]),
-                        pack_bf16x2(st[rb + 4], st[rb + 5]), pack_bf16x2(st[rb + 6], st[rb + 7])};
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
       const char* vt = vbuf + 16 * t * C::ROWB;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
@@ -259,15 +260,70 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
         const bf16x4 lo = lds_read_tr(vt + vrow1 * C::ROWB + ((ch ^ vsw1) << 4) + vbyte);
         const bf16x4 hi = lds_read_tr(vt + vrow2 * C::ROWB + ((ch ^ vsw2) << 4) + vbyte);
         const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t], o[dt], 0, 0, 0);
       }
     }
+  };
 
-    if (more) {
-      char* nk = smem + ((j + 1 - j0) & 1) * 2 * C::BLKB;
-      lstore(nk, nk + C::BLKB);
+  // Software pipeline over the split's key blocks [j0, j1).  Step j holds the raw scores
+  // of block j in registers and, in LDS, K of block j+1 and V of block j.  It starts the
+  // loads of K(j+2) and V(j+1) into the slots freed by step j-1, settles the running max,
+  // computes the scores of block j+1 (MFMA) alongside the exponentials of block j (VALU),
+  // then O += V(j)^T P(j)^T, waits for its loads and meets the other waves at the barrier.
+  auto kslot = [&](int i) { return smem + i * C::BLKB; };
+  auto vslot = [&](int i) { return smem + (2 + i) * C::BLKB; };
+  const int j0 = split * a.kvb_per_split;
+  const int j1 = min(j0 + a.kvb_per_split, nkv);
+  f32x16 s_a[2], s_b[2];
+  bf16x8 pb[4];
+  dload(kb, kslot(0), j0 * C::BN);
+  dload(vb, vslot(0), j0 * C::BN);
+  if (j0 + 1 < j1) dload(kb, kslot(1), (j0 + 1) * C::BN);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk(kslot(0), s_a);
+  __syncthreads();  // K slot 0 is refilled by the first step
+
+  auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
+    const int r = j - j0;
+    if (j + 2 < j1) dload(kb, kslot(r & 1), (j + 2) * C::BN);
+    dload(vb, vslot((r + 1) & 1), (j + 1) * C::BN);
+    rescale(s_cur, j * C::BN, false);
+    qk(kslot((r + 1) & 1), s_nxt);
+    exp_pack(s_cur, pb, j * C::BN, false);
+    pv(vslot(r & 1), pb);
+    // interleave: each score MFMA with its operand read and a slice of the exponentials,
+    // then each PV MFMA with the two transposing reads of its operand
+#pragma unroll
+    for (int i = 0; i < 2 * C::KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 112 / (2 * C::KS), 0);  // VALU + TRANS
     }
+#pragma unroll
+    for (int i = 0; i < 4 * C::DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  int j = j0;
+  for (; j + 2 < j1; j += 2) {
+    step(j, s_a, s_b);
+    step(j + 1, s_b, s_a);
+  }
+  if (j + 1 < j1) {
+    step(j, s_a, s_b);
+    ++j;
+    s_a[0] = s_b[0];
+    s_a[1] = s_b[1];
+  }
+  {
+    const bool tail = (j + 1) * C::BN > S;
+    rescale(s_a, j * C::BN, tail);
+    exp_pack(s_a, pb, j * C::BN, tail);
+    pv(vslot((j - j0) & 1), pb);
   }
 
   // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
@@ -285,19 +341,17 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
           r[(dt * 4 + q4) * 64] = f32x4{o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
       r[(PREC - 1) * 64] = f32x4{m_run, l_run, 0.f, 0.f};
     }
-    // Each wave's stores complete (workgroup-scope release), then ONE device-scope release
-    // for the whole workgroup before its arrival is counted: a device-scope fence writes
-    // back the XCD's L2, which is far too costly to repeat per wave.
+    // The partials and counters are in uncached memory: once this wave's stores have
+    // completed they are visible device-wide, and the counter is updated at memory.  A
+    // workgroup-scope release (wait for the stores) and the barrier order them before the
+    // arrival count; the reads below bypass every cache.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       const uint32_t prev = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int is_last = prev == (uint32_t)(a.n_split - 1);
-      if (is_last) {
-        __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other splits' partials
-      }
+      if (is_last) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_flag = is_last;
     }
     __syncthreads();
@@ -349,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   // read once as wave-uniform (scalar) values: the stores then issue back to back with no
   // wait between them.  Tiny slabs (fewer than 32 rows) take a per-row-pointer path.
   constexpr int NST = 32 * C::CH / 64;  // 16-byte stores per lane
-  const int wu = __builtin_amdgcn_readfirstlane(w);
+  // wu: this wave's index as a wave-uniform value (defined with the loads above)
   const int row0 = m0 + wu * 32;
   if (row0 >= S) return;
   const int rowN = min(row0 + 31, S - 1);
