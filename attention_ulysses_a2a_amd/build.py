@@ -51,6 +51,12 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    # A kernel template whose host-side instantiation fails is dropped silently by the
+    # host pass (its launch stub stays undefined); refuse such a library here.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "xstage" in ln]
+    if missing:
+        raise RuntimeError(f"libxstage.so has undefined symbols of its own: {missing}")
     os.replace(tmp, LIB)
     return LIB
 

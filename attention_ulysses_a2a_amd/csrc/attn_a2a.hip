@@ -131,55 +131,83 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   // K/V blocks go from global memory straight into LDS (global_load_lds_dwordx4: no
   // registers).  One instruction of wave w fills the 1 KiB LDS segment (i*4 + w) of a
   // block, lane by lane, so each lane fetches the global chunk that belongs at its LDS slot
-  // under the swizzle.  Keys past the end are clamped to row S-1: their scores are masked
-  // and their weights set to exactly zero, so the duplicated (finite) rows add nothing.
+  // under the swizzle.  The block base is wave-uniform (scalar registers) and each lane's
+  // offset within a block is fixed, so a load costs no vector ALU work.  Keys past the end
+  // (last block only) are clamped to row S-1: their scores are masked and their weights set
+  // to exactly zero, so the duplicated (finite) rows add nothing.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  uint32_t ld_off[C::NLD];  // element offset of this lane's chunk within a key block
-  int ld_row[C::NLD];
+  uint32_t ld_lane[C::NLD];  // element offset of this lane's chunk from the block's first key
+  auto ld_row = [&](int i) { return ((i * 4 + w) * 64 + lane) / C::CH; };
 #pragma unroll
   for (int i = 0; i < C::NLD; ++i) {
     const int P = (i * 4 + w) * 64 + lane;
     const int row = P / C::CH, pc = P % C::CH;
-    ld_row[i] = row;
-    ld_off[i] = (uint32_t)((pc ^ swz<D>(row)) * 8);
+    ld_lane[i] = (uint32_t)row * rs + (uint32_t)((pc ^ swz<D>(row)) * 8);
   }
-  auto dload = [&](const uint16_t* src, char* dst, int n0) {
+  auto dload = [&](const uint16_t* src, int slot_byte, int n0) {
+    if (n0 + C::BN <= S) {
+      const uint16_t* base = src + (uint32_t)n0 * rs;
 #pragma unroll
-    for (int i = 0; i < C::NLD; ++i) {
-      const int key = min(n0 + ld_row[i], S - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(src + (uint32_t)key * rs + ld_off[i]),
-                                       (__attribute__((address_space(3))) void*)(dst + (i * 4 + wu) * 1024), 16, 0, 0);
+      for (int i = 0; i < C::NLD; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(base + ld_lane[i]),
+                                         (__attribute__((address_space(3))) void*)(smem + slot_byte + (i * 4 + wu) * 1024),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::NLD; ++i) {
+        const int row = ld_row(i);
+        const int key = min(n0 + row, S - 1);
+        const uint32_t off = ld_lane[i] + (uint32_t)(key - row) * rs;  // = key * rs + chunk offset
+        __builtin_amdgcn_global_load_lds((const void*)(src + off),
+                                         (__attribute__((address_space(3))) void*)(smem + slot_byte + (i * 4 + wu) * 1024),
+                                         16, 0, 0);
+      }
     }
   };
 
-  // Per-lane LDS offsets (loop invariant).
+  // LDS slots: K at byte 0 and BLKB, V at 2*BLKB and 3*BLKB.  Every per-lane read address
+  // below is a fixed per-lane base plus a compile-time offset (slot, tile), so the reads
+  // carry their offsets as immediates.
+  constexpr int KSLOT0 = 0, VSLOT0 = 2 * C::BLKB;
   const int krow = lane & 31;
   const int kswz = swz<D>(krow);
+  int kaddr[C::KS];  // score A operand: row krow, logical chunk 2ks + hl
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) kaddr[ks] = krow * C::ROWB + (((2 * ks + hl) ^ kswz) << 4);
   // transposing V reads: lane group g = lane/16, s4 = lane%16
-  const int g = lane >> 4, s4 = lane & 15;
-  const int vrow1 = 4 * (g >> 1) + (s4 >> 2);
-  const int vrow2 = vrow1 + 8;
-  const int vc0 = 2 * (g & 1) + ((s4 & 3) >> 1);  // chunk within a 32-wide d tile
-  const int vbyte = (s4 & 1) * 8;
-  const int vsw1 = swz<D>(vrow1), vsw2 = swz<D>(vrow2);
+  int vaddr[C::DT][2];
+  {
+    const int g = lane >> 4, s4 = lane & 15;
+    const int vrow1 = 4 * (g >> 1) + (s4 >> 2);
+    const int vrow2 = vrow1 + 8;
+    const int vc0 = 2 * (g & 1) + ((s4 & 3) >> 1);  // chunk within a 32-wide d tile
+    const int vbyte = (s4 & 1) * 8;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      vaddr[dt][0] = vrow1 * C::ROWB + (((4 * dt + vc0) ^ swz<D>(vrow1)) << 4) + vbyte;
+      vaddr[dt][1] = vrow2 * C::ROWB + (((4 * dt + vc0) ^ swz<D>(vrow2)) << 4) + vbyte;
+    }
+  }
 
   f32x16 o[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY;
   float l_run = 0.f;
-  const float c = a.c;
+  // c = |scale| log2(e), kept >= FLT_MIN so that a masked score (-inf) * c stays -inf; for
+  // scale = 0 every real score times FLT_MIN is below 2^-100 in magnitude, so all weights
+  // are exp2(0) = 1 in fp32 exactly as with c = 0.
+  const float c = __builtin_fmaxf(a.c, 1.17549435e-38f);
 
-  // S^T = K Q^T for one 64-key block held in LDS (two 32-key tiles)
-  auto qk = [&](const char* kbuf, f32x16* st) {
+  // S^T = K Q^T for one 64-key block held in K slot `ks_byte` (two 32-key tiles)
+  auto qk = [&](int ks_byte, f32x16* st) {
     st[0] = f32x16{};
     st[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const char* p = kbuf + (t * 32 + krow) * C::ROWB + (((2 * ks + hl) ^ kswz) << 4);
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(p);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + kaddr[ks] + ks_byte + t * 32 * C::ROWB);
         st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[t], 0, 0, 0);
       }
     }
@@ -190,8 +218,10 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   //  * rescale(): block max; the running max is only raised when the block exceeds it by
   //    more than kLazy (log2 units), so weights stay below 2^kLazy (exact after the final
   //    division) and the O rescale, one multiply per accumulator, is skipped for most blocks;
-  //  * exp_pack(): weights, row sums, and bf16 packing into the B operand of the PV MFMA.
-  // Keys past S exist only in the very last block (`tail`): masked out of the max, weight 0.
+  //  * exp_pack(): weights, bf16 packing into the B operand of the PV MFMA, and the row sum
+  //    of the packed (bf16) weights, i.e. of exactly the weights the PV product uses.
+  // Keys past S exist only in the very last block (`tail`): their scores become -inf, so
+  // they drop out of the max and get weight exp2(-inf) = 0 (c > 0 always, see below).
   constexpr float kLazy = 8.0f;
   const int nkv = (S + C::BN - 1) / C::BN;
   auto key_of = [&](int n0, int t, int r) { return n0 + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3); };
@@ -203,16 +233,12 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
         for (int r = 0; r < 16; ++r)
           if (key_of(n0, t, r) >= S) st[t][r] = -INFINITY;
     }
-    float m4[4];
+    float mx = __builtin_fmaxf(st[0][0], st[0][1]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x16& x = st[q >> 1];
-      const int r0 = (q & 1) * 8;
-      const float u = __builtin_fmaxf(__builtin_fmaxf(x[r0], x[r0 + 1]), __builtin_fmaxf(x[r0 + 2], x[r0 + 3]));
-      const float v = __builtin_fmaxf(__builtin_fmaxf(x[r0 + 4], x[r0 + 5]), __builtin_fmaxf(x[r0 + 6], x[r0 + 7]));
-      m4[q] = __builtin_fmaxf(u, v);
-    }
-    const float mx = max_with_partner32(__builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3]))) * c;
+    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, st[0][r]), st[0][r + 1]);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, st[1][r]), st[1][r + 1]);
+    mx = max_with_partner32(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
       const float m_new = __builtin_fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -222,43 +248,40 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
       m_run = m_new;
     }
   };
-  auto exp_pack = [&](f32x16* st, bf16x8* pb, int n0, bool tail) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  auto exp_pack = [&](f32x16* st, bf16x8* pb) {
     const float neg_m = -m_run;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][r], c, neg_m));
-    if (tail) {  // (-inf) * c is NaN when scale == 0: zero the masked weights explicitly
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key_of(n0, t, r) >= S) st[t][r] = 0.f;
-    }
-    float rs4[4];
+    float rsum = l_run;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x16& x = st[q >> 1];
       const int r0 = (q & 1) * 8;
-      rs4[q] = ((x[r0] + x[r0 + 1]) + (x[r0 + 2] + x[r0 + 3])) + ((x[r0 + 4] + x[r0 + 5]) + (x[r0 + 6] + x[r0 + 7]));
-      const u32x4 pk = {pack_bf16x2(x[r0 + 0], x[r0 + 1]), pack_bf16x2(x[r0 + 2], x[r0 + 3]),
-                        pack_bf16x2(x[r0 + 4], x[r0 + 5]), pack_bf16x2(x[r0 + 6], x[r0 + 7])};
-      pb[q] = __builtin_bit_cast(bf16x8, pk);
+      // (each packed word goes to the dot product as its own value: feeding it as an element
+      // of the 4-word vector has been miscompiled into four dot products of the first word)
+      const uint32_t w0 = pack_bf16x2(x[r0 + 0], x[r0 + 1]), w1 = pack_bf16x2(x[r0 + 2], x[r0 + 3]);
+      const uint32_t w2 = pack_bf16x2(x[r0 + 4], x[r0 + 5]), w3 = pack_bf16x2(x[r0 + 6], x[r0 + 7]);
+      rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, rsum, false);
+      rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, rsum, false);
+      rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, rsum, false);
+      rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, rsum, false);
+      pb[q] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
     }
-    l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+    l_run = rsum;
   };
 
   // O^T += V^T P^T, four 16-key steps; k-step t uses pb[t] = registers 8*(t&1)..+7 of the
   // score tile t>>1, i.e. keys 16t + 8*(jj/4) + 4*hl + jj%4 for slot jj.
-  auto pv = [&](const char* vbuf, const bf16x8* pb) {
+  auto pv = [&](int vs_byte, const bf16x8* pb) {
 #pragma unroll
     for (int t = 0; t < C::BN / 16; ++t) {
-      const char* vt = vbuf + 16 * t * C::ROWB;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const int ch = 4 * dt + vc0;
-        const bf16x4 lo = lds_read_tr(vt + vrow1 * C::ROWB + ((ch ^ vsw1) << 4) + vbyte);
-        const bf16x4 hi = lds_read_tr(vt + vrow2 * C::ROWB + ((ch ^ vsw2) << 4) + vbyte);
+        const bf16x4 lo = lds_read_tr(smem + vaddr[dt][0] + vs_byte + 16 * t * C::ROWB);
+        const bf16x4 hi = lds_read_tr(smem + vaddr[dt][1] + vs_byte + 16 * t * C::ROWB);
         const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t], o[dt], 0, 0, 0);
       }
@@ -270,60 +293,45 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   // loads of K(j+2) and V(j+1) into the slots freed by step j-1, settles the running max,
   // computes the scores of block j+1 (MFMA) alongside the exponentials of block j (VALU),
   // then O += V(j)^T P(j)^T, waits for its loads and meets the other waves at the barrier.
-  auto kslot = [&](int i) { return smem + i * C::BLKB; };
-  auto vslot = [&](int i) { return smem + (2 + i) * C::BLKB; };
+  // Slot parity alternates with j - j0; the loop is unrolled by two so it is static.
   const int j0 = split * a.kvb_per_split;
   const int j1 = min(j0 + a.kvb_per_split, nkv);
   f32x16 s_a[2], s_b[2];
   bf16x8 pb[4];
-  dload(kb, kslot(0), j0 * C::BN);
-  dload(vb, vslot(0), j0 * C::BN);
-  if (j0 + 1 < j1) dload(kb, kslot(1), (j0 + 1) * C::BN);
+  dload(kb, KSLOT0, j0 * C::BN);
+  dload(vb, VSLOT0, j0 * C::BN);
+  if (j0 + 1 < j1) dload(kb, KSLOT0 + C::BLKB, (j0 + 1) * C::BN);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  qk(kslot(0), s_a);
+  qk(KSLOT0, s_a);
   __syncthreads();  // K slot 0 is refilled by the first step
 
-  auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
-    const int r = j - j0;
-    if (j + 2 < j1) dload(kb, kslot(r & 1), (j + 2) * C::BN);
-    dload(vb, vslot((r + 1) & 1), (j + 1) * C::BN);
+  // PAR = (j - j0) & 1 is a literal at every call, so after inlining the slot offsets fold.
+  auto step = [&](int j, const int PAR, f32x16* s_cur, f32x16* s_nxt) {
+    if (j + 2 < j1) dload(kb, KSLOT0 + PAR * C::BLKB, (j + 2) * C::BN);
+    dload(vb, VSLOT0 + (1 - PAR) * C::BLKB, (j + 1) * C::BN);
     rescale(s_cur, j * C::BN, false);
-    qk(kslot((r + 1) & 1), s_nxt);
-    exp_pack(s_cur, pb, j * C::BN, false);
-    pv(vslot(r & 1), pb);
-    // interleave: each score MFMA with its operand read and a slice of the exponentials,
-    // then each PV MFMA with the two transposing reads of its operand
-#pragma unroll
-    for (int i = 0; i < 2 * C::KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 112 / (2 * C::KS), 0);  // VALU + TRANS
-    }
-#pragma unroll
-    for (int i = 0; i < 4 * C::DT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
+    qk(KSLOT0 + (1 - PAR) * C::BLKB, s_nxt);
+    exp_pack(s_cur, pb);
+    pv(VSLOT0 + PAR * C::BLKB, pb);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
   int j = j0;
   for (; j + 2 < j1; j += 2) {
-    step(j, s_a, s_b);
-    step(j + 1, s_b, s_a);
+    step(j, 0, s_a, s_b);
+    step(j + 1, 1, s_b, s_a);
   }
+  const bool tail = j1 * C::BN > S;
   if (j + 1 < j1) {
-    step(j, s_a, s_b);
-    ++j;
-    s_a[0] = s_b[0];
-    s_a[1] = s_b[1];
-  }
-  {
-    const bool tail = (j + 1) * C::BN > S;
+    step(j, 0, s_a, s_b);
+    rescale(s_b, (j + 1) * C::BN, tail);
+    exp_pack(s_b, pb);
+    pv(VSLOT0 + C::BLKB, pb);
+  } else {
     rescale(s_a, j * C::BN, tail);
-    exp_pack(s_a, pb, j * C::BN, tail);
-    pv(vslot((j - j0) & 1), pb);
+    exp_pack(s_a, pb);
+    pv(VSLOT0, pb);
   }
 
   // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
