@@ -85,6 +85,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
+  // The body names device-only types (the buffer resource), which the host pass of a
+  // template cannot instantiate; the host pass only needs the launch signature.
+#if defined(__HIP_DEVICE_COMPILE__)
   using C = AttnCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[4 * C::BLKB];  // K0 V0 K1 V1
 
@@ -128,41 +131,30 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     }
   }
 
-  // K/V blocks go from global memory straight into LDS (global_load_lds_dwordx4: no
+  // K/V blocks go from global memory straight into LDS (buffer_load_dwordx4 ... lds: no
   // registers).  One instruction of wave w fills the 1 KiB LDS segment (i*4 + w) of a
   // block, lane by lane, so each lane fetches the global chunk that belongs at its LDS slot
-  // under the swizzle.  The block base is wave-uniform (scalar registers) and each lane's
-  // offset within a block is fixed, so a load costs no vector ALU work.  Keys past the end
-  // (last block only) are clamped to row S-1: their scores are masked and their weights set
-  // to exactly zero, so the duplicated (finite) rows add nothing.
+  // under the swizzle.  The buffer resource spans the S rows of this (b, h): the block
+  // offset is a scalar, each lane's offset within a block is fixed, and rows past the end
+  // of the sequence read as zeros (hardware range check) — no clamping, no branches.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  uint32_t ld_lane[C::NLD];  // element offset of this lane's chunk from the block's first key
-  auto ld_row = [&](int i) { return ((i * 4 + w) * 64 + lane) / C::CH; };
+  const int head_bytes = (int)((uint32_t)S * rs * 2u);
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, head_bytes, 0x00020000);
+  uint32_t ld_voff[C::NLD];  // byte offset of this lane's chunk from the block's first key
 #pragma unroll
   for (int i = 0; i < C::NLD; ++i) {
     const int P = (i * 4 + w) * 64 + lane;
     const int row = P / C::CH, pc = P % C::CH;
-    ld_lane[i] = (uint32_t)row * rs + (uint32_t)((pc ^ swz<D>(row)) * 8);
+    ld_voff[i] = ((uint32_t)row * rs + (uint32_t)((pc ^ swz<D>(row)) * 8)) * 2u;
   }
-  auto dload = [&](const uint16_t* src, int slot_byte, int n0) {
-    if (n0 + C::BN <= S) {
-      const uint16_t* base = src + (uint32_t)n0 * rs;
+  auto dload = [&](const __amdgpu_buffer_rsrc_t& rsrc, int slot_byte, int n0) {
+    const uint32_t soff = (uint32_t)n0 * rs * 2u;
 #pragma unroll
-      for (int i = 0; i < C::NLD; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(base + ld_lane[i]),
-                                         (__attribute__((address_space(3))) void*)(smem + slot_byte + (i * 4 + wu) * 1024),
-                                         16, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::NLD; ++i) {
-        const int row = ld_row(i);
-        const int key = min(n0 + row, S - 1);
-        const uint32_t off = ld_lane[i] + (uint32_t)(key - row) * rs;  // = key * rs + chunk offset
-        __builtin_amdgcn_global_load_lds((const void*)(src + off),
-                                         (__attribute__((address_space(3))) void*)(smem + slot_byte + (i * 4 + wu) * 1024),
-                                         16, 0, 0);
-      }
-    }
+    for (int i = 0; i < C::NLD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(smem + slot_byte + (i * 4 + wu) * 1024), 16, ld_voff[i],
+          soff, 0, 0);
   };
 
   // LDS slots: K at byte 0 and BLKB, V at 2*BLKB and 3*BLKB.  Every per-lane read address
@@ -221,24 +213,26 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   //  * exp_pack(): weights, bf16 packing into the B operand of the PV MFMA, and the row sum
   //    of the packed (bf16) weights, i.e. of exactly the weights the PV product uses.
   // Keys past S exist only in the very last block (`tail`): their scores become -inf, so
-  // they drop out of the max and get weight exp2(-inf) = 0 (c > 0 always, see below).
+  // they drop out of the max and get weight exp2(-inf) = 0 (c > 0 always, see above).
   constexpr float kLazy = 8.0f;
   const int nkv = (S + C::BN - 1) / C::BN;
   auto key_of = [&](int n0, int t, int r) { return n0 + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3); };
-  auto rescale = [&](f32x16* st, int n0, bool tail) {
-    if (tail) {
+  auto mask_tail = [&](f32x16* st, int n0) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key_of(n0, t, r) >= S) st[t][r] = -INFINITY;
-    }
+      for (int r = 0; r < 16; ++r)
+        if (key_of(n0, t, r) >= S) st[t][r] = -INFINITY;
+  };
+  auto blockmax = [&](const f32x16* st) {
     float mx = __builtin_fmaxf(st[0][0], st[0][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, st[0][r]), st[0][r + 1]);
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, st[1][r]), st[1][r + 1]);
-    mx = max_with_partner32(mx) * c;
+    return max_with_partner32(mx) * c;
+  };
+  auto rescale_to = [&](float mx) {
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
       const float m_new = __builtin_fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -255,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][r], c, neg_m));
-    float rsum = l_run;
+    float rs4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x16& x = st[q >> 1];
@@ -264,13 +258,13 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
       // of the 4-word vector has been miscompiled into four dot products of the first word)
       const uint32_t w0 = pack_bf16x2(x[r0 + 0], x[r0 + 1]), w1 = pack_bf16x2(x[r0 + 2], x[r0 + 3]);
       const uint32_t w2 = pack_bf16x2(x[r0 + 4], x[r0 + 5]), w3 = pack_bf16x2(x[r0 + 6], x[r0 + 7]);
-      rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, rsum, false);
-      rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, rsum, false);
-      rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, rsum, false);
-      rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, rsum, false);
+      float r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.f, false);
+      r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, r, false);
+      r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, r, false);
+      rs4[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, r, false);
       pb[q] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
     }
-    l_run = rsum;
+    l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
   };
 
   // O^T += V^T P^T, four 16-key steps; k-step t uses pb[t] = registers 8*(t&1)..+7 of the
@@ -289,31 +283,52 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   };
 
   // Software pipeline over the split's key blocks [j0, j1).  Step j holds the raw scores
-  // of block j in registers and, in LDS, K of block j+1 and V of block j.  It starts the
-  // loads of K(j+2) and V(j+1) into the slots freed by step j-1, settles the running max,
-  // computes the scores of block j+1 (MFMA) alongside the exponentials of block j (VALU),
-  // then O += V(j)^T P(j)^T, waits for its loads and meets the other waves at the barrier.
-  // Slot parity alternates with j - j0; the loop is unrolled by two so it is static.
+  // of block j (and their max) in registers and, in LDS, K of block j+1 and V of block j.
+  // It starts the loads of K(j+2) and V(j+1) into the slots freed by step j-1, settles the
+  // running max, computes the scores of block j+1 (MFMA) alongside the exponentials of
+  // block j (VALU), then O += V(j)^T P(j)^T alongside the max of block j+1, waits for its
+  // loads and meets the other waves at the barrier.  Slot parity alternates with j - j0;
+  // the loop is unrolled by two so it is static.  Rows past S (zeros) are only in the last
+  // block, handled after the loop: there the max is recomputed with those keys at -inf.
   const int j0 = split * a.kvb_per_split;
   const int j1 = min(j0 + a.kvb_per_split, nkv);
   f32x16 s_a[2], s_b[2];
   bf16x8 pb[4];
-  dload(kb, KSLOT0, j0 * C::BN);
-  dload(vb, VSLOT0, j0 * C::BN);
-  if (j0 + 1 < j1) dload(kb, KSLOT0 + C::BLKB, (j0 + 1) * C::BN);
+  float mx;
+  dload(krsrc, KSLOT0, j0 * C::BN);
+  dload(vrsrc, VSLOT0, j0 * C::BN);
+  if (j0 + 1 < j1) dload(krsrc, KSLOT0 + C::BLKB, (j0 + 1) * C::BN);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   qk(KSLOT0, s_a);
+  mx = blockmax(s_a);
   __syncthreads();  // K slot 0 is refilled by the first step
 
   // PAR = (j - j0) & 1 is a literal at every call, so after inlining the slot offsets fold.
   auto step = [&](int j, const int PAR, f32x16* s_cur, f32x16* s_nxt) {
-    if (j + 2 < j1) dload(kb, KSLOT0 + PAR * C::BLKB, (j + 2) * C::BN);
-    dload(vb, VSLOT0 + (1 - PAR) * C::BLKB, (j + 1) * C::BN);
-    rescale(s_cur, j * C::BN, false);
+    if (j + 2 < j1) dload(krsrc, KSLOT0 + PAR * C::BLKB, (j + 2) * C::BN);
+    dload(vrsrc, VSLOT0 + (1 - PAR) * C::BLKB, (j + 1) * C::BN);
+    rescale_to(mx);
     qk(KSLOT0 + (1 - PAR) * C::BLKB, s_nxt);
     exp_pack(s_cur, pb);
     pv(VSLOT0 + PAR * C::BLKB, pb);
+    mx = blockmax(s_nxt);
+    // Interleave: score MFMAs with operand reads kept 4 ahead and the exponentials; then
+    // the PV MFMAs with their transposing reads kept two MFMAs ahead and the next max.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + 4 < 2 * C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * C::DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + 2 < 4 * C::DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
@@ -323,15 +338,20 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     step(j + 1, 1, s_b, s_a);
   }
   const bool tail = j1 * C::BN > S;
+  auto last_block = [&](int jl, f32x16* st, int vs_byte) {
+    if (tail) {
+      mask_tail(st, jl * C::BN);
+      mx = blockmax(st);
+    }
+    rescale_to(mx);
+    exp_pack(st, pb);
+    pv(vs_byte, pb);
+  };
   if (j + 1 < j1) {
     step(j, 0, s_a, s_b);
-    rescale(s_b, (j + 1) * C::BN, tail);
-    exp_pack(s_b, pb);
-    pv(VSLOT0 + C::BLKB, pb);
+    last_block(j + 1, s_b, VSLOT0 + C::BLKB);
   } else {
-    rescale(s_a, j * C::BN, tail);
-    exp_pack(s_a, pb);
-    pv(VSLOT0, pb);
+    last_block(j, s_a, VSLOT0);
   }
 
   // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
@@ -456,6 +476,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
       }
     }
   }
+#endif
 }
 
 template <int D>
