@@ -385,25 +385,47 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     __syncthreads();
     if (!last_flag) return;
     // Merge in split order from memory (own partial included), so the result does not
-    // depend on which split arrived last.
-    float m_all = -INFINITY;
-    for (int sp = 0; sp < a.n_split; ++sp) m_all = __builtin_fmaxf(m_all, rec(sp)[(PREC - 1) * 64][0]);
+    // depend on which split arrived last.  Uncached reads have a long latency, so every
+    // (m, l) is requested at once, and each split's O chunks are in flight while the
+    // previous split is accumulated.
+    constexpr int MAXS = 16;
+    float ms[MAXS], ls[MAXS];
+#pragma unroll
+    for (int sp = 0; sp < MAXS; ++sp) {
+      const f32x4 ml = sp < a.n_split ? rec(sp)[(PREC - 1) * 64] : f32x4{-INFINITY, 0.f, 0.f, 0.f};
+      ms[sp] = ml[0];
+      ls[sp] = ml[1];
+    }
+    float m_all = ms[0];
+#pragma unroll
+    for (int sp = 1; sp < MAXS; ++sp) m_all = __builtin_fmaxf(m_all, ms[sp]);
     l_run = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x16{};
+    constexpr int NCH = 4 * C::DT;
+    f32x4 cur[NCH], nxt[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) cur[ch] = rec(0)[ch * 64];
     for (int sp = 0; sp < a.n_split; ++sp) {
-      const f32x4* r = rec(sp);
-      const f32x4 ml = r[(PREC - 1) * 64];
-      const float f = __builtin_amdgcn_exp2f(ml[0] - m_all);
-      l_run += ml[1] * f;
+      if (sp + 1 < a.n_split) {
+        const f32x4* r = rec(sp + 1);
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) nxt[ch] = r[ch * 64];
+      }
+      float msp = ms[0], lsp = ls[0];
+#pragma unroll
+      for (int k = 1; k < MAXS; ++k)
+        if (sp == k) msp = ms[k], lsp = ls[k];
+      const float f = __builtin_amdgcn_exp2f(msp - m_all);
+      l_run += lsp * f;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 x = r[(dt * 4 + q4) * 64];
+        for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[dt][4 * q4 + e] += x[e] * f;
-        }
+          for (int e = 0; e < 4; ++e) o[dt][4 * q4 + e] += cur[dt * 4 + q4][e] * f;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) cur[ch] = nxt[ch];
     }
     m_run = m_all;
   }
