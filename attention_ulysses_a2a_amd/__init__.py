@@ -38,6 +38,7 @@ __all__ = [
     "xstage_wallclock_hz",
     "xstage_bg_t_iss",
     "xstage_status_str",
+    "bind",
     "LibraryMissing",
     "XStageError",
 ]
@@ -176,3 +177,73 @@ def xstage_bg_t_iss(G_s: float, T0_s: float, V_bytes: float, R_bytes_per_s: floa
 
 def xstage_status_str(status: int) -> str:
     return lib().xstage_status_str(int(status)).decode()
+
+
+class _Bound:
+    """A prepared launch: one C call with arguments marshalled once (see ``bind``)."""
+
+    __slots__ = ("_fn", "_args", "_name", "_refs")
+
+    def __init__(self, fn, args, name, refs):
+        self._fn, self._args, self._name, self._refs = fn, args, name, refs
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != XSTAGE_OK:
+            raise XStageError(st, self._name)
+
+
+def bind(name: str, *args, **kwargs) -> _Bound:
+    """Validates and marshals the arguments of entry point ``name`` once and returns a
+    zero-argument callable that issues that call.
+
+    Meant for launch loops (benchmarks, serving steps), where the per-call Python checks
+    would otherwise cost about as much host time as a short kernel takes on the GPU.  The
+    bound buffers are kept alive by the callable; the stream is fixed at bind time (the
+    current stream of the tensors' device unless ``stream`` is given), and the calls must be
+    made with that device current.  Supported: xstage_attn_a2a_fwd, xstage_attn_fwd,
+    xstage_a2a_scatter, xstage_attn_a2a_unfused, with the same arguments as the functions.
+    """
+    import torch
+
+    L = lib()
+    if name == "xstage_attn_a2a_fwd":
+        q, k, v, out_slabs = args[:4]
+        scale, stream = kwargs.get("scale", args[4] if len(args) > 4 else None), kwargs.get("stream")
+        B, S, H, D = _qkv(q, k, v)
+        ptrs, P = _slab_ptrs(out_slabs)
+        arr, keep = ptr_array(ptrs)
+        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), _stream_of(q, stream))
+        refs, dev = (q, k, v, out_slabs, keep), q.device
+    elif name == "xstage_attn_fwd":
+        q, k, v, out = args[:4]
+        scale, stream = kwargs.get("scale", args[4] if len(args) > 4 else None), kwargs.get("stream")
+        B, S, H, D = _qkv(q, k, v)
+        _dev_tensor(out, "out")
+        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, H, D, _scale(scale, D),
+                _stream_of(q, stream))
+        refs, dev = (q, k, v, out), q.device
+    elif name == "xstage_a2a_scatter":
+        inp, out_slabs = args[:2]
+        stream = kwargs.get("stream")
+        _dev_tensor(inp, "in")
+        B, S, H, D = (int(x) for x in inp.shape)
+        ptrs, P = _slab_ptrs(out_slabs)
+        arr, keep = ptr_array(ptrs)
+        call = (inp.data_ptr(), arr, B, S, H, D, P, _stream_of(inp, stream))
+        refs, dev = (inp, out_slabs, keep), inp.device
+    elif name == "xstage_attn_a2a_unfused":
+        q, k, v, workspace, out_slabs = args[:5]
+        scale, stream = kwargs.get("scale", args[5] if len(args) > 5 else None), kwargs.get("stream")
+        B, S, H, D = _qkv(q, k, v)
+        _dev_tensor(workspace, "workspace")
+        ptrs, P = _slab_ptrs(out_slabs)
+        arr, keep = ptr_array(ptrs)
+        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), workspace.data_ptr(), arr, B, S, H, D, P,
+                _scale(scale, D), _stream_of(q, stream))
+        refs, dev = (q, k, v, workspace, out_slabs, keep), q.device
+    else:
+        raise ValueError(f"bind: unsupported entry point {name!r}")
+    if torch.cuda.current_device() != dev.index:
+        raise ValueError(f"bind: make {dev} the current device first")
+    return _Bound(getattr(L, name), call, name, refs)

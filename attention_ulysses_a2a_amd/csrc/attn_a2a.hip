@@ -67,7 +67,7 @@ struct AttnArgs {
   int kvb_per_split; // 64-key blocks per split
   float c;           // |scale| * log2(e): scores are turned into base-2 logits
   uint32_t qflip;    // 0x80008000 for a negative scale: Q is negated on load
-  f32x4* partial;    // split partials: [tile][split][wave][PREC chunks][64 lanes] (n_split > 1)
+  f32x4* partial;    // split partials: [tile][split][wave][chunk][64 lanes] (n_split > 1)
   uint32_t* counters;  // per-tile arrival counters, zero between launches (n_split > 1)
 };
 
@@ -355,19 +355,30 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   }
 
   // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
-  // merges them (exact rescaling by exp2(m_s - m)) and runs the epilogue for the tile.
+  // merges them (rescaling by exp2(m_s - m)) and runs the epilogue for the tile.
   if (a.n_split > 1) {
     __shared__ int last_flag;
-    constexpr int PREC = 4 * C::DT + 1;  // 16-byte chunks per lane: O registers, then (m, l)
+    // One record per (tile, split, wave), in lane-major 16-byte chunks: the unnormalised O
+    // rounded to bf16 (two chunks per 32-wide d tile, accumulator registers 0..7 and 8..15),
+    // then (m, l) in fp32.  bf16 halves the bytes written here and read back by the merge,
+    // both of which sit on the tail of the kernel; the rounding adds at most one bf16 unit
+    // in the last place relative to each partial, inside the output's own rounding scale.
+    constexpr int OCH = 2 * C::DT;
+    constexpr int PREC = OCH + 1;
     auto rec = [&](int sp) { return a.partial + ((size_t)(tile * a.n_split + sp) * 4 + w) * PREC * 64 + lane; };
     {
       f32x4* r = rec(split);
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          r[(dt * 4 + q4) * 64] = f32x4{o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
-      r[(PREC - 1) * 64] = f32x4{m_run, l_run, 0.f, 0.f};
+        for (int hh = 0; hh < 2; ++hh) {
+          const f32x16& x = o[dt];
+          const int e0 = 8 * hh;
+          const u32x4 v = {pack_bf16x2(x[e0 + 0], x[e0 + 1]), pack_bf16x2(x[e0 + 2], x[e0 + 3]),
+                           pack_bf16x2(x[e0 + 4], x[e0 + 5]), pack_bf16x2(x[e0 + 6], x[e0 + 7])};
+          reinterpret_cast<u32x4*>(r)[(2 * dt + hh) * 64] = v;
+        }
+      r[OCH * 64] = f32x4{m_run, l_run, 0.f, 0.f};
     }
     // The partials and counters are in uncached memory: once this wave's stores have
     // completed they are visible device-wide, and the counter is updated at memory.  A
@@ -384,50 +395,56 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     }
     __syncthreads();
     if (!last_flag) return;
-    // Merge in split order from memory (own partial included), so the result does not
-    // depend on which split arrived last.  Uncached reads have a long latency, so every
-    // (m, l) is requested at once, and each split's O chunks are in flight while the
-    // previous split is accumulated.
-    constexpr int MAXS = 16;
-    float ms[MAXS], ls[MAXS];
-#pragma unroll
-    for (int sp = 0; sp < MAXS; ++sp) {
-      const f32x4 ml = sp < a.n_split ? rec(sp)[(PREC - 1) * 64] : f32x4{-INFINITY, 0.f, 0.f, 0.f};
-      ms[sp] = ml[0];
-      ls[sp] = ml[1];
-    }
-    float m_all = ms[0];
-#pragma unroll
-    for (int sp = 1; sp < MAXS; ++sp) m_all = __builtin_fmaxf(m_all, ms[sp]);
-    l_run = 0.f;
+    // Merge in split order (own partial included, read back from memory), so the result does
+    // not depend on which split arrived last.  Uncached reads have a long latency: the
+    // records of NB splits are requested together and folded in with a running-max rescale,
+    // so that up to NB splits cost one round trip.
+    constexpr int NB = 4;
+    float m_acc = -INFINITY, l_acc = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x16{};
-    constexpr int NCH = 4 * C::DT;
-    f32x4 cur[NCH], nxt[NCH];
+    for (int s0 = 0; s0 < a.n_split; s0 += NB) {
+      u32x4 ob[NB][OCH];
+      f32x4 ml[NB];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) cur[ch] = rec(0)[ch * 64];
-    for (int sp = 0; sp < a.n_split; ++sp) {
-      if (sp + 1 < a.n_split) {
-        const f32x4* r = rec(sp + 1);
+      for (int i = 0; i < NB; ++i) {
+        if (s0 + i < a.n_split) {
+          const f32x4* r = rec(s0 + i);
+          ml[i] = r[OCH * 64];
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) nxt[ch] = r[ch * 64];
+          for (int ch = 0; ch < OCH; ++ch) ob[i][ch] = reinterpret_cast<const u32x4*>(r)[ch * 64];
+        } else {
+          ml[i] = f32x4{-INFINITY, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ch = 0; ch < OCH; ++ch) ob[i][ch] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
-      float msp = ms[0], lsp = ls[0];
+      float m_new = m_acc;
 #pragma unroll
-      for (int k = 1; k < MAXS; ++k)
-        if (sp == k) msp = ms[k], lsp = ls[k];
-      const float f = __builtin_amdgcn_exp2f(msp - m_all);
-      l_run += lsp * f;
+      for (int i = 0; i < NB; ++i) m_new = __builtin_fmaxf(m_new, ml[i][0]);
+      const float fo = m_acc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_acc - m_new);
+      l_acc *= fo;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+      for (int dt = 0; dt < C::DT; ++dt) o[dt] *= fo;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
+      for (int i = 0; i < NB; ++i) {
+        const float f = __builtin_amdgcn_exp2f(ml[i][0] - m_new);
+        l_acc += ml[i][1] * f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[dt][4 * q4 + e] += cur[dt * 4 + q4][e] * f;
+        for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) cur[ch] = nxt[ch];
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t wv = ob[i][2 * dt + hh][k];
+              o[dt][8 * hh + 2 * k] += __uint_as_float(wv << 16) * f;
+              o[dt][8 * hh + 2 * k + 1] += __uint_as_float(wv & 0xffff0000u) * f;
+            }
+      }
+      m_acc = m_new;
     }
-    m_run = m_all;
+    m_run = m_acc;
+    l_run = l_acc;
   }
 
   // ---- epilogue: normalise, bf16, restage per wave, store rows into their slabs ----------
@@ -525,8 +542,9 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
 }
 
-// Bytes of split partials for one tile and one split (4 waves x PREC chunks x 64 lanes x 16 B).
-static size_t partial_bytes_per_unit(int D) { return (size_t)4 * (4 * (D / 32) + 1) * 64 * 16; }
+// Bytes of split partials for one tile and one split: 4 waves x (2 bf16 O chunks per 32-wide
+// d tile + one (m, l) chunk) x 64 lanes x 16 B.
+static size_t partial_bytes_per_unit(int D) { return (size_t)4 * (2 * (D / 32) + 1) * 64 * 16; }
 
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
                     int P, float scale, hipStream_t stream) {

@@ -204,3 +204,29 @@ def test_burst_gap_stamps_and_payload():
         assert np.all(words[s, :, :, 0] == tid[None, :])
         assert np.all(words[s, :, :, 1] == np.arange(K, dtype=np.uint32)[:, None])
         assert np.all(words[s, :, :, 2] == 0x5A5A5A5A) and np.all(words[s, :, :, 3] == 0xA5A5A5A5)
+
+
+def test_bound_launches_equal_direct_calls():
+    """xs.bind(...) issues the same C calls: outputs equal the direct calls bit for bit, also
+    over repeated launches (split counters and workspace reused between calls)."""
+    w = workload("flux1024")
+    qb, kb, vb = make_inputs(w)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    ref = run_fused(w, qb, kb, vb, w.scale).slabs_host()
+    g = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
+    fused = xs.bind("xstage_attn_a2a_fwd", q, k, v, g.views, w.scale)
+    for _ in range(3):
+        fused()
+    torch.cuda.synchronize()
+    assert g.guards_intact() and np.array_equal(g.slabs_host(), ref)
+    ws = torch.empty((w.B, w.S, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    g2 = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
+    xs.bind("xstage_attn_a2a_unfused", q, k, v, ws, g2.views, w.scale)()
+    torch.cuda.synchronize()
+    assert g2.guards_intact() and np.array_equal(g2.slabs_host(), ref)
+    out = torch.empty((w.B, w.S, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    xs.bind("xstage_attn_fwd", q, k, v, out, w.scale)()
+    g3 = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
+    xs.bind("xstage_a2a_scatter", out, g3.views)()
+    torch.cuda.synchronize()
+    assert np.array_equal(g3.slabs_host(), ref)
