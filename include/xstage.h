@@ -28,13 +28,22 @@
  *     into the kernel arguments, so the array may be freed as soon as the call returns.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work and return;
  *     they never synchronize.  Except where stated, they never allocate or free memory.
+ *   - Workspace (attention entry points): when a shape is split along the keys across
+ *     workgroups (small B*H*S), the first such call on a (device, stream) allocates one
+ *     library-owned uncached workspace (320 MiB of partial results, 4 MiB of counters,
+ *     zeroed with one device synchronization) that lives until the process ends; later calls
+ *     on that (device, stream) reuse it and allocate nothing.  Calls on one stream are
+ *     ordered, so they never share it concurrently; calls on different streams use
+ *     different workspaces.  A shape whose partials exceed the capacity is refused with
+ *     XSTAGE_ERR_UNSUPPORTED before any launch.
  *   - Errors: every argument check runs before any HIP call; on an error nothing is
  *     launched and no output byte is touched.  Faults inside kernels surface at the
  *     caller's next synchronization.  XSTAGE_ERR_HIP reports the HIP launch status.
  *   - Attention: O = softmax(scale * Q K^T) V per (b, h), non-causal, products and sums in
  *     fp32, output rounded to bf16 (round to nearest, ties to even).  scale may be any
  *     finite value, including 0 and negative values.
- *   - Thread safety: entry points hold no mutable state and may be called concurrently.
+ *   - Thread safety: the only mutable state is the per-(device, stream) workspace table,
+ *     guarded by a mutex; entry points may be called concurrently.
  */
 #ifndef XSTAGE_H_
 #define XSTAGE_H_
