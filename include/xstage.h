@@ -34,8 +34,8 @@
  *     zeroed with one device synchronization) that lives until the process ends; later calls
  *     on that (device, stream) reuse it and allocate nothing.  Calls on one stream are
  *     ordered, so they never share it concurrently; calls on different streams use
- *     different workspaces.  A shape whose partials exceed the capacity is refused with
- *     XSTAGE_ERR_UNSUPPORTED before any launch.
+ *     different workspaces.  A shape is split only as far as its partials fit the
+ *     workspace; a failed allocation returns XSTAGE_ERR_HIP before any launch.
  *   - Errors: every argument check runs before any HIP call; on an error nothing is
  *     launched and no output byte is touched.  Faults inside kernels surface at the
  *     caller's next synchronization.  XSTAGE_ERR_HIP reports the HIP launch status.
