@@ -366,6 +366,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     constexpr int OCH = 2 * C::DT;
     constexpr int PREC = OCH + 1;
     auto rec = [&](int sp) { return a.partial + ((size_t)(tile * a.n_split + sp) * 4 + w) * PREC * 64 + lane; };
+    u32x4 own[OCH];  // this split's record, kept for the merge should it arrive last
     {
       f32x4* r = rec(split);
 #pragma unroll
@@ -374,12 +375,13 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
         for (int hh = 0; hh < 2; ++hh) {
           const f32x16& x = o[dt];
           const int e0 = 8 * hh;
-          const u32x4 v = {pack_bf16x2(x[e0 + 0], x[e0 + 1]), pack_bf16x2(x[e0 + 2], x[e0 + 3]),
-                           pack_bf16x2(x[e0 + 4], x[e0 + 5]), pack_bf16x2(x[e0 + 6], x[e0 + 7])};
-          reinterpret_cast<u32x4*>(r)[(2 * dt + hh) * 64] = v;
+          own[2 * dt + hh] = u32x4{pack_bf16x2(x[e0 + 0], x[e0 + 1]), pack_bf16x2(x[e0 + 2], x[e0 + 3]),
+                                   pack_bf16x2(x[e0 + 4], x[e0 + 5]), pack_bf16x2(x[e0 + 6], x[e0 + 7])};
+          reinterpret_cast<u32x4*>(r)[(2 * dt + hh) * 64] = own[2 * dt + hh];
         }
       r[OCH * 64] = f32x4{m_run, l_run, 0.f, 0.f};
     }
+    const f32x4 own_ml = {m_run, l_run, 0.f, 0.f};
     // The partials and counters are in uncached memory: once this wave's stores have
     // completed they are visible device-wide, and the counter is updated at memory.  A
     // workgroup-scope release (wait for the stores) and the barrier order them before the
@@ -395,8 +397,8 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     }
     __syncthreads();
     if (!last_flag) return;
-    // Merge in split order (own partial included, read back from memory), so the result does
-    // not depend on which split arrived last.  Uncached reads have a long latency: the
+    // Merge in split order (own partial included, as the bits of its record), so the result
+    // does not depend on which split arrived last.  Uncached reads have a long latency: the
     // records of NB splits are requested together and folded in with a running-max rescale,
     // so that up to NB splits cost one round trip.
     constexpr int NB = 4;
@@ -408,7 +410,11 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
       f32x4 ml[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        if (s0 + i < a.n_split) {
+        if (s0 + i == split) {  // own record: the same bits, from registers
+          ml[i] = own_ml;
+#pragma unroll
+          for (int ch = 0; ch < OCH; ++ch) ob[i][ch] = own[ch];
+        } else if (s0 + i < a.n_split) {
           const f32x4* r = rec(s0 + i);
           ml[i] = r[OCH * 64];
 #pragma unroll
