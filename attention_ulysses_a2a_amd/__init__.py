@@ -34,6 +34,8 @@ __all__ = [
     "xstage_attn_fwd",
     "xstage_a2a_scatter",
     "xstage_attn_a2a_unfused",
+    "xstage_attn_a2a_plan",
+    "xstage_attn_a2a_fwd_traced",
     "xstage_burst_gap_run",
     "xstage_wallclock_hz",
     "xstage_bg_t_iss",
@@ -149,6 +151,32 @@ def xstage_attn_a2a_unfused(q, k, v, workspace, out_slabs, scale=None, stream=No
     _check(st, "xstage_attn_a2a_unfused")
 
 
+def xstage_attn_a2a_plan(B: int, S: int, H_local: int, D: int):
+    """(n_workgroups, n_split) of the attention launch for this shape on the current device."""
+    nwg, nsp = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().xstage_attn_a2a_plan(int(B), int(S), int(H_local), int(D), ctypes.byref(nwg), ctypes.byref(nsp)),
+           "xstage_attn_a2a_plan")
+    return nwg.value, nsp.value
+
+
+def xstage_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, stream=None) -> None:
+    """Instrumented fused call (store-span study); ``stamps`` is an int64 device tensor of
+    n_workgroups * 16 entries (xstage_attn_a2a_plan); modes as in include/xstage.h."""
+    import torch
+
+    B, S, H, D = _qkv(q, k, v)
+    ptrs, P = _slab_ptrs(out_slabs)
+    nwg, _ = xstage_attn_a2a_plan(B, S, H, D)
+    if not stamps.is_cuda or stamps.element_size() != 8 or stamps.numel() < nwg * 16 or not stamps.is_contiguous():
+        raise ValueError(f"stamps must be a contiguous 64-bit device tensor of >= {nwg * 16} entries")
+    arr, keep = ptr_array(ptrs)
+    with torch.cuda.device(q.device):
+        st = lib().xstage_attn_a2a_fwd_traced(q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P,
+                                              _scale(scale, D), int(mode), stamps.data_ptr(), _stream_of(q, stream))
+    del keep
+    _check(st, "xstage_attn_a2a_fwd_traced")
+
+
 def xstage_burst_gap_run(K, V_bytes, gap_fma_iters, rounds, dst, stamps, n_dst_sets=1, nontemporal=False,
                          stream=None) -> None:
     """Burst-Gap store microbenchmark; ``stamps`` is an int64 device tensor of K*rounds*3 entries."""
@@ -242,6 +270,15 @@ def bind(name: str, *args, **kwargs) -> _Bound:
         call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), workspace.data_ptr(), arr, B, S, H, D, P,
                 _scale(scale, D), _stream_of(q, stream))
         refs, dev = (q, k, v, workspace, out_slabs, keep), q.device
+    elif name == "xstage_attn_a2a_fwd_traced":
+        q, k, v, out_slabs, mode, stamps = args[:6]
+        scale, stream = kwargs.get("scale", args[6] if len(args) > 6 else None), kwargs.get("stream")
+        B, S, H, D = _qkv(q, k, v)
+        ptrs, P = _slab_ptrs(out_slabs)
+        arr, keep = ptr_array(ptrs)
+        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), int(mode),
+                stamps.data_ptr(), _stream_of(q, stream))
+        refs, dev = (q, k, v, out_slabs, stamps, keep), q.device
     else:
         raise ValueError(f"bind: unsupported entry point {name!r}")
     if torch.cuda.current_device() != dev.index:

@@ -7,7 +7,8 @@
 
 namespace xstage {
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
-                    int P, float scale, hipStream_t stream);
+                    int P, float scale, hipStream_t stream, int mode = 0, unsigned long long* stamps = nullptr);
+int attn_workgroups(int B, int S, int H, int D, int* n_split);
 int launch_scatter(const void* in, const SlabTable& slabs, int B, int S, int H, int D, int P, hipStream_t stream);
 int launch_burst_gap(const xstage_bg_params_t& p, hipStream_t stream);
 
@@ -77,6 +78,32 @@ int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* w
   st = launch_attn_any(q, k, v, make_table(one, 1), B, S, H_local, D, 1, scale, s);
   if (st != XSTAGE_OK) return st;
   return launch_scatter(workspace, make_table(out_slabs, P), B, S, H_local, D, P, s);
+}
+
+int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_split) {
+  if (n_workgroups == nullptr) return XSTAGE_ERR_INVALID;
+  const int st = check_shape(B, S, H_local, D, 1);
+  if (st != XSTAGE_OK) return st;
+  *n_workgroups = attn_workgroups(B, S, H_local, D, n_split);
+  return XSTAGE_OK;
+}
+
+int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
+                               int H_local, int D, int P, float scale, int mode, unsigned long long* stamps,
+                               void* stream) {
+  if (mode < 0 || mode > 2 || stamps == nullptr || (reinterpret_cast<uintptr_t>(stamps) & 7u) != 0)
+    return XSTAGE_ERR_INVALID;
+  int st = check_shape(B, S, H_local, D, P);
+  if (st != XSTAGE_OK) return st;
+  const unsigned long long stamp_bytes = (unsigned long long)attn_workgroups(B, S, H_local, D, nullptr) * 16ull * 8ull;
+  const Range sr = range_of(stamps, stamp_bytes);
+  const unsigned long long tb = tensor_bytes(B, S, H_local, D);
+  if (q && (overlaps(sr, range_of(q, tb)) || overlaps(sr, range_of(k, tb)) || overlaps(sr, range_of(v, tb))))
+    return XSTAGE_ERR_INVALID;
+  st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, stamps, stamp_bytes);
+  if (st != XSTAGE_OK) return st;
+  return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale,
+                         static_cast<hipStream_t>(stream), 1 + mode, stamps);
 }
 
 int xstage_burst_gap_run(const xstage_bg_params_t* p, void* stream) {

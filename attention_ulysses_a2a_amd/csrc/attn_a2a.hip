@@ -69,7 +69,16 @@ struct AttnArgs {
   uint32_t qflip;    // 0x80008000 for a negative scale: Q is negated on load
   f32x4* partial;    // split partials: [tile][split][wave][chunk][64 lanes] (n_split > 1)
   uint32_t* counters;  // per-tile arrival counters, zero between launches (n_split > 1)
+  unsigned long long* stamps;  // traced modes: [workgroup][wave][4] wall-clock ticks
 };
+
+// Kernel modes.  kRun is the product path.  The traced modes record, per wave, the
+// wall-clock time at start, at the end of the key loop, after the last epilogue store was
+// issued and (kCoupled) after those stores completed: kTraced changes nothing else;
+// kCoupled makes every wave wait for its stores before it ends (the completion-coupled
+// counterfactual: the issuer blocks until its stores are visible); kNoStore issues no output
+// store at all (the unbounded-asynchronous bound: stores cost nothing; nothing is written).
+enum AttnMode { kRun = 0, kTraced = 1, kCoupled = 2, kNoStore = 3 };
 
 // A pointer read through a wave-uniform index, kept in scalar registers.
 __device__ __forceinline__ uint16_t* uniform_ptr(uint16_t* p) {
@@ -83,7 +92,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   // The body names device-only types (the buffer resource), which the host pass of a
   // template cannot instantiate; the host pass only needs the launch signature.
@@ -95,6 +104,19 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int hl = lane >> 5;  // half of the wave
+  unsigned long long t_start = 0, t_loop = 0;
+  if constexpr (MODE != kRun) t_start = __builtin_amdgcn_s_memrealtime();
+  auto trace_out = [&](unsigned long long t_issued, unsigned long long t_done) {
+    if constexpr (MODE != kRun) {
+      if (lane == 0) {
+        unsigned long long* st = a.stamps + ((size_t)blockIdx.x * 4 + w) * 4;
+        st[0] = t_start;
+        st[1] = t_loop;
+        st[2] = t_issued;
+        st[3] = t_done;
+      }
+    }
+  };
 
   // XCD-aware unit order: workgroup i runs on XCD i % 8; give each XCD a contiguous range
   // of (b, h, m-tile) units so that one head's K/V stays in one XCD's L2.
@@ -354,6 +376,8 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     last_block(j, s_a, VSLOT0);
   }
 
+  if constexpr (MODE != kRun) t_loop = __builtin_amdgcn_s_memrealtime();
+
   // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
   // merges them (rescaling by exp2(m_s - m)) and runs the epilogue for the tile.
   if (a.n_split > 1) {
@@ -396,7 +420,10 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
       last_flag = is_last;
     }
     __syncthreads();
-    if (!last_flag) return;
+    if (!last_flag) {
+      trace_out(0, 0);
+      return;
+    }
     // Merge in split order (own partial included, as the bits of its record), so the result
     // does not depend on which split arrived last.  Uncached reads have a long latency: the
     // records of NB splits are requested together and folded in with a running-max rescale,
@@ -478,7 +505,10 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   constexpr int NST = 32 * C::CH / 64;  // 16-byte stores per lane
   // wu: this wave's index as a wave-uniform value (defined with the loads above)
   const int row0 = m0 + wu * 32;
-  if (row0 >= S) return;
+  if (row0 >= S || MODE == kNoStore) {
+    trace_out(0, 0);
+    return;
+  }
   const int rowN = min(row0 + 31, S - 1);
   const int p_lo = row0 / a.S_P, p_hi = rowN / a.S_P;
   const bool full = row0 + 31 < S;
@@ -521,12 +551,22 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
       }
     }
   }
+  if constexpr (MODE != kRun) {
+    const unsigned long long t_issued = __builtin_amdgcn_s_memrealtime();
+    unsigned long long t_done = 0;
+    if constexpr (MODE == kCoupled) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      t_done = __builtin_amdgcn_s_memrealtime();
+    }
+    trace_out(t_issued, t_done);
+  }
 #endif
 }
 
 template <int D>
 static int launch_attn(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H,
-                       int P, float scale, const SplitPlan& plan, hipStream_t stream) {
+                       int P, float scale, const SplitPlan& plan, int mode, unsigned long long* stamps,
+                       hipStream_t stream) {
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -544,7 +584,14 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.qflip = std::signbit(scale) ? 0x80008000u : 0u;
   a.partial = static_cast<f32x4*>(plan.partial);
   a.counters = plan.counters;
-  hipLaunchKernelGGL(attn_a2a_kernel<D>, dim3(a.n_units), dim3(AttnCfg<D>::THREADS), 0, stream, a);
+  a.stamps = stamps;
+  const dim3 grid(a.n_units), block(AttnCfg<D>::THREADS);
+  switch (mode) {
+    case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced>), grid, block, 0, stream, a); break;
+    case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled>), grid, block, 0, stream, a); break;
+    case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun>), grid, block, 0, stream, a); break;
+  }
   return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
 }
 
@@ -552,8 +599,15 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
 // d tile + one (m, l) chunk) x 64 lanes x 16 B.
 static size_t partial_bytes_per_unit(int D) { return (size_t)4 * (2 * (D / 32) + 1) * 64 * 16; }
 
+int attn_workgroups(int B, int S, int H, int D, int* n_split) {
+  const int n_tiles = B * H * ((S + 127) / 128);
+  const SplitPlan plan = choose_split(n_tiles, (S + 63) / 64, partial_bytes_per_unit(D));
+  if (n_split) *n_split = plan.n_split;
+  return n_tiles * plan.n_split;
+}
+
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
-                    int P, float scale, hipStream_t stream) {
+                    int P, float scale, hipStream_t stream, int mode, unsigned long long* stamps) {
   const int n_tiles = B * H * ((S + 127) / 128);
   const int nkv = (S + 63) / 64;
   SplitPlan plan = choose_split(n_tiles, nkv, partial_bytes_per_unit(D));
@@ -562,8 +616,8 @@ int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable
                                      &plan.partial, &plan.counters);
     if (st != XSTAGE_OK) return st;
   }
-  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, stream);
-  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, stream);
+  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, stream);
+  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, stream);
 }
 
 }  // namespace xstage

@@ -1,0 +1,115 @@
+"""Per-tile store spans of the fused epilogue and its overhead against sequence length.
+
+X-Stage explainer (gist.science, arXiv 2607.23264), technical summary, "Results",
+FlashAttention-A2A: as the sequence grows, the next tile's key loop covers the drain of the
+previous tile's stores, the fused kernel approaches attention alone, and the overhead stays
+flat, contradicting a completion-coupled counterfactual whose overhead grows linearly with
+the sequence; "Contributions", X-Stage item: neither a fully blocking nor an unbounded
+asynchronous model describes the issuer.
+
+On one GPU the stores go to local HBM.  For each sequence length this measures (HIP events,
+back-to-back launches, inputs resident):
+  * t_attn      attention alone, contiguous output (xstage_attn_fwd);
+  * t_fused     the fused kernel (xstage_attn_a2a_fwd);
+  * t_nostore   the unbounded-asynchronous bound: the traced kernel issuing no output store;
+  * t_coupled   the completion-coupled counterfactual: every wave waits for its stores;
+and, from the traced kernel's per-wave stamps, the epilogue span (end of the key loop to the
+last store issued; includes the merge of key splits) and, in the coupled mode, the drain
+span (last store issued to stores complete).  The completion-coupled model predicts
+t_fused + rounds * drain, with rounds = workgroups per co-resident slot.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+
+import numpy as np
+
+DEFAULT_S = (1024, 2304, 4608, 9216, 16896, 32760)
+
+
+def coupled_prediction(t_fused_s: float, rounds: float, drain_s: float) -> float:
+    """Completion-coupled counterfactual: each of the `rounds` workgroup generations of a
+    slot additionally waits for its stores to drain."""
+    return t_fused_s + rounds * drain_s
+
+
+def spans_from_stamps(stamps: np.ndarray, hz: float):
+    """stamps: [n_workgroups, 4 waves, 4] ticks -> (epilogue spans, drain spans) in seconds,
+    over the waves that stored output."""
+    st = stamps.reshape(-1, 4).astype(np.int64)
+    emit = st[:, 2] > 0
+    epi = (st[emit, 2] - st[emit, 1]) / hz
+    done = emit & (st[:, 3] > 0)
+    drain = (st[done, 3] - st[done, 2]) / hz
+    return epi, drain
+
+
+def _time(torch, fn, n, warm):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n * 1e-3
+
+
+def run_study(torch, xs, S_list=DEFAULT_S, H=3, D=128, P=8, seed=11, target_s=0.05, slots=None, emit=print):
+    from synth import Workload, make_inputs
+
+    hz = xs.xstage_wallclock_hz()
+    if slots is None:
+        slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    rows = []
+    for S in S_list:
+        S = (S // P) * P
+        w = Workload(f"study{S}", 1, S, H, D, P, seed=seed)
+        qb, kb, vb = make_inputs(w)
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+        q, k, v = dev(qb), dev(kb), dev(vb)
+        slabs = torch.empty((P, 1, S // P, H, D), dtype=torch.bfloat16, device="cuda")
+        sl = [slabs[p] for p in range(P)]
+        out1 = torch.empty((1, S, H, D), dtype=torch.bfloat16, device="cuda")
+        nwg, nsp = xs.xstage_attn_a2a_plan(1, S, H, D)
+        stamps = [torch.zeros(nwg * 16, dtype=torch.int64, device="cuda") for _ in range(3)]
+        calls = {
+            "attn": xs.bind("xstage_attn_fwd", q, k, v, out1, w.scale),
+            "fused": xs.bind("xstage_attn_a2a_fwd", q, k, v, sl, w.scale),
+            "traced": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 0, stamps[0], w.scale),
+            "coupled": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 1, stamps[1], w.scale),
+            "nostore": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 2, stamps[2], w.scale),
+        }
+        t_est = _time(torch, calls["fused"], 3, 3)
+        n = max(20, min(2000, int(target_s / max(t_est, 1e-6))))
+        t = {name: _time(torch, fn, n, max(50, n // 4)) for name, fn in calls.items()}
+        epi, _ = spans_from_stamps(stamps[0].cpu().numpy(), hz)
+        _, drain = spans_from_stamps(stamps[1].cpu().numpy(), hz)
+        rounds = nwg / slots
+        drain_med = float(np.median(drain)) if len(drain) else 0.0
+        row = {
+            "S": S, "H_local": H, "D": D, "P": P, "workgroups": nwg, "key_splits": nsp, "rounds": round(rounds, 3),
+            "t_attn_us": t["attn"] * 1e6, "t_fused_us": t["fused"] * 1e6, "t_traced_us": t["traced"] * 1e6,
+            "t_nostore_us": t["nostore"] * 1e6, "t_coupled_us": t["coupled"] * 1e6,
+            "overhead_fused_vs_attn_us": (t["fused"] - t["attn"]) * 1e6,
+            "overhead_fused_vs_nostore_us": (t["fused"] - t["nostore"]) * 1e6,
+            "overhead_coupled_vs_nostore_us": (t["coupled"] - t["nostore"]) * 1e6,
+            "epilogue_span_us_median": float(np.median(epi)) * 1e6 if len(epi) else None,
+            "epilogue_span_us_p90": float(np.percentile(epi, 90)) * 1e6 if len(epi) else None,
+            "drain_span_us_median": drain_med * 1e6,
+            "drain_span_us_p90": float(np.percentile(drain, 90)) * 1e6 if len(drain) else None,
+            "coupled_model_us": coupled_prediction(t["fused"], math.ceil(rounds), drain_med) * 1e6,
+            "iterations": n,
+        }
+        rows.append(row)
+        emit(json.dumps(row))
+        del q, k, v, slabs, out1, stamps, calls
+        torch.cuda.empty_cache()
+    return rows

@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--bg", action="store_true", help="run the Burst-Gap store sweep instead")
+    ap.add_argument("--xstage-study", action="store_true",
+                    help="fused-epilogue overhead and store spans against sequence length (one JSON line per S)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the scatter kernel on a 512 MiB input (reference for HBM byte counters)")
     return ap.parse_args()
@@ -219,6 +221,11 @@ def main():
         from attention_ulysses_a2a_amd.bg_sweep import run_sweep
 
         run_sweep(torch, xs)
+        return
+    if args.xstage_study:
+        from attention_ulysses_a2a_amd.xstage_study import run_study
+
+        run_study(torch, xs, emit=lambda line: print(line, flush=True))
         return
     if args.copy_calibration:
         # B=1, S=262144, H=8, D=128, P=8: 512 MiB read and 512 MiB written per call; the

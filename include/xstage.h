@@ -90,6 +90,32 @@ int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* w
                             void* const* out_slabs, int B, int S, int H_local, int D, int P,
                             float scale, void* stream);
 
+/* Work decomposition of the attention entry points for this shape on the current device:
+ * *n_workgroups workgroups of 4 waves (n_tiles x key splits, n_tiles = B * H_local *
+ * ceil(S / 128)), *n_split key splits per 128-row tile (n_split may be NULL).  Host only;
+ * sizes the stamps of xstage_attn_a2a_fwd_traced. */
+int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_split);
+
+/* Instrumented xstage_attn_a2a_fwd for the per-tile store-span study ("Results",
+ * FlashAttention-A2A: the measured overhead against the completion-coupled counterfactual;
+ * "Contributions", X-Stage item: neither a fully blocking nor an unbounded asynchronous
+ * model describes the issuer).  Same arguments and the same slab contents as
+ * xstage_attn_a2a_fwd, plus:
+ *   mode 0: nothing else changes (the stores of a tile are not waited on);
+ *   mode 1: completion-coupled counterfactual: each wave waits for its epilogue stores to
+ *           complete before it ends;
+ *   mode 2: unbounded-asynchronous bound: no output store is issued at all (the slabs are
+ *           NOT written; everything else runs);
+ *   stamps: device uint64 [n_workgroups][4 waves][4] (xstage_attn_a2a_plan), caller-owned,
+ *           8-byte aligned, disjoint from every other argument; per wave, in wall-clock
+ *           ticks (xstage_wallclock_hz): start, end of the key loop, last epilogue store
+ *           issued (0 if the wave stores nothing: a split that does not merge, rows past S,
+ *           mode 2), stores complete (mode 1 only, else 0).
+ * Other modes are XSTAGE_ERR_INVALID. */
+int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void* const* out_slabs,
+                               int B, int S, int H_local, int D, int P, float scale, int mode,
+                               unsigned long long* stamps, void* stream);
+
 /* Burst-Gap store microbenchmark ("Methodology"; "Contributions", characterisation item).
  * K producer workgroups (256 threads each) run `rounds` rounds of: a burst that stores
  * V_bytes / K bytes as 16-byte stores into the producer's share of destination set

@@ -46,7 +46,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -149,6 +149,36 @@ def test_unfused_rejects(L):
     assert f(Q, K, V, SLAB0 + GAP - 64, arr, 1, 256, 2, 64, 2, 0.125, None) == INVALID  # overlaps slab 1
     assert f(Q, K, V, W, arr, 1, 256, 2, 64, 2, float("nan"), None) == INVALID
     assert f(Q, K, V, W, arr, 1, 256, 2, 64, 3, 0.125, None) == INVALID
+
+
+def test_plan_counts_workgroups(L):
+    """Host-only: the decomposition the traced call's stamps are sized by."""
+    nwg, nsp = xs.xstage_attn_a2a_plan(1, 4608, 3, 128)
+    assert nwg % nsp == 0 and nwg // nsp == 3 * 36 and 1 <= nsp <= 16
+    nwg, nsp = xs.xstage_attn_a2a_plan(1, 1, 1, 64)
+    assert (nwg, nsp) == (1, 1)
+    n = _lib.ctypes.c_int(0)
+    assert L.xstage_attn_a2a_plan(1, 256, 2, 80, _lib.ctypes.byref(n), None) == UNSUPPORTED
+    assert L.xstage_attn_a2a_plan(0, 256, 2, 64, _lib.ctypes.byref(n), None) == INVALID
+    assert L.xstage_attn_a2a_plan(1, 256, 2, 64, None, None) == INVALID
+
+
+STAMPS = 0x50_0000_0000
+
+
+@no_device
+def test_traced_rejects(L):
+    arr, keep = _lib.ptr_array(slabs(2))
+    f = L.xstage_attn_a2a_fwd_traced
+    args = (Q, K, V, arr, 1, 256, 2, 64, 2, 0.125)
+    assert f(*args, 3, STAMPS, None) == INVALID                # unknown mode
+    assert f(*args, -1, STAMPS, None) == INVALID
+    assert f(*args, 0, 0, None) == INVALID                     # no stamps
+    assert f(*args, 0, STAMPS + 4, None) == INVALID            # misaligned stamps
+    assert f(*args, 0, Q + 64, None) == INVALID                # stamps inside q
+    assert f(*args, 0, SLAB0 + 64, None) == INVALID            # stamps inside a slab
+    assert f(Q, K, V, arr, 1, 256, 2, 64, 2, float("nan"), 0, STAMPS, None) == INVALID
+    assert f(Q, K, V, arr, 1, 255, 2, 64, 2, 0.125, 0, STAMPS, None) == INVALID
 
 
 @no_device

@@ -230,3 +230,36 @@ def test_bound_launches_equal_direct_calls():
     xs.bind("xstage_a2a_scatter", out, g3.views)()
     torch.cuda.synchronize()
     assert np.array_equal(g3.slabs_host(), ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux1024"])
+def test_traced_modes(name):
+    """The instrumented call: modes 0 and 1 write the fused result bit for bit, mode 2 writes
+    nothing; per-wave stamps are ordered, and exactly the waves owning output rows of a
+    merged (or unsplit) tile record a store."""
+    w = workload(name)
+    qb, kb, vb = make_inputs(w)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    ref = run_fused(w, qb, kb, vb, w.scale).slabs_host()
+    nwg, nsp = xs.xstage_attn_a2a_plan(w.B, w.S, w.H, w.D)
+    for mode in (0, 1, 2):
+        g = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
+        stamps = torch.zeros(nwg * 16, dtype=torch.int64, device="cuda")
+        xs.xstage_attn_a2a_fwd_traced(q, k, v, g.views, mode, stamps, w.scale)
+        torch.cuda.synchronize()
+        assert g.guards_intact()
+        if mode == 2:
+            assert np.all(g.slabs_host() == NAN_BF16)
+        else:
+            assert np.array_equal(g.slabs_host(), ref), mode
+        st = stamps.cpu().numpy().reshape(nwg, 4, 4)
+        assert np.all(st[:, :, 0] > 0) and np.all(st[:, :, 1] >= st[:, :, 0])
+        emit = st[:, :, 2] > 0
+        assert np.all(st[emit][:, 2] >= st[emit][:, 1])
+        n_tiles = nwg // nsp
+        row_waves = sum(min(4, -(-(w.S - 128 * (t % (n_tiles // (w.B * w.H)))) // 32)) for t in range(n_tiles))
+        assert emit.sum() == (0 if mode == 2 else row_waves), (mode, emit.sum(), row_waves)
+        if mode == 1:
+            assert np.all(st[emit][:, 3] >= st[emit][:, 2]) and np.all(st[emit][:, 3] > 0)
+        else:
+            assert np.all(st[:, :, 3] == 0)
