@@ -601,7 +601,7 @@ static size_t partial_bytes_per_unit(int D) { return (size_t)4 * (2 * (D / 32) +
 
 int attn_workgroups(int B, int S, int H, int D, int* n_split) {
   const int n_tiles = B * H * ((S + 127) / 128);
-  const SplitPlan plan = choose_split(n_tiles, (S + 63) / 64, partial_bytes_per_unit(D));
+  const SplitPlan plan = choose_split(n_tiles, (S + 63) / 64, D, partial_bytes_per_unit(D));
   if (n_split) *n_split = plan.n_split;
   return n_tiles * plan.n_split;
 }
@@ -610,7 +610,7 @@ int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable
                     int P, float scale, hipStream_t stream, int mode, unsigned long long* stamps) {
   const int n_tiles = B * H * ((S + 127) / 128);
   const int nkv = (S + 63) / 64;
-  SplitPlan plan = choose_split(n_tiles, nkv, partial_bytes_per_unit(D));
+  SplitPlan plan = choose_split(n_tiles, nkv, D, partial_bytes_per_unit(D));
   if (plan.n_split > 1) {
     const int st = acquire_workspace(stream, (size_t)n_tiles * plan.n_split * partial_bytes_per_unit(D), n_tiles,
                                      &plan.partial, &plan.counters);

@@ -15,10 +15,10 @@ struct SplitPlan {
   uint32_t* counters = nullptr;  // n_tiles arrival counters, zero between launches
 };
 
-// Picks the split count that minimises (rounds of co-resident workgroups) x (key blocks per
-// workgroup) plus a small merge charge, for `n_tiles` tiles of 128 query rows over `nkv`
-// blocks of 64 keys, on the current device (2 workgroups per compute unit).
-SplitPlan choose_split(int n_tiles, int nkv, size_t partial_bytes_per_unit);
+// Picks the key-split count of `n_tiles` tiles of 128 query rows over `nkv` blocks of 64
+// keys (head dimension D) on the current device, from a cost model of rounds of
+// co-resident workgroups (two per compute unit) and of the merge of split tiles.
+SplitPlan choose_split(int n_tiles, int nkv, int D, size_t partial_bytes_per_unit);
 
 // Returns buffers of at least `partial_bytes` and `n_counters` zeroed counters owned by the
 // library for (current device, stream).  Grows them on demand: growing synchronizes
