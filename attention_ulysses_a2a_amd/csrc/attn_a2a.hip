@@ -98,7 +98,17 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   // template cannot instantiate; the host pass only needs the launch signature.
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = AttnCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * C::BLKB];  // K0 V0 K1 V1
+  // K0 K1 V0 V1 as four LDS objects rather than one array: the compiler then knows that the
+  // reads of one slot do not alias the asynchronous global->LDS copies into another, and
+  // does not wait for those copies before every read.  Slots are named by the byte offsets
+  // they would have in one array (compile-time constants after inlining).
+  __shared__ __attribute__((aligned(16))) char lds_k0[C::BLKB];
+  __shared__ __attribute__((aligned(16))) char lds_k1[C::BLKB];
+  __shared__ __attribute__((aligned(16))) char lds_v0[C::BLKB];
+  __shared__ __attribute__((aligned(16))) char lds_v1[C::BLKB];
+  auto sp = [&](int slot_byte) -> char* {
+    return slot_byte < C::BLKB ? lds_k0 : slot_byte < 2 * C::BLKB ? lds_k1 : slot_byte < 3 * C::BLKB ? lds_v0 : lds_v1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -175,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(smem + slot_byte + (i * 4 + wu) * 1024), 16, ld_voff[i],
+          rsrc, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16, ld_voff[i],
           soff, 0, 0);
   };
 
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + kaddr[ks] + ks_byte + t * 32 * C::ROWB);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sp(ks_byte) + kaddr[ks] + t * 32 * C::ROWB);
         st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[t], 0, 0, 0);
       }
     }
@@ -296,8 +306,8 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     for (int t = 0; t < C::BN / 16; ++t) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const bf16x4 lo = lds_read_tr(smem + vaddr[dt][0] + vs_byte + 16 * t * C::ROWB);
-        const bf16x4 hi = lds_read_tr(smem + vaddr[dt][1] + vs_byte + 16 * t * C::ROWB);
+        const bf16x4 lo = lds_read_tr(sp(vs_byte) + vaddr[dt][0] + 16 * t * C::ROWB);
+        const bf16x4 hi = lds_read_tr(sp(vs_byte) + vaddr[dt][1] + 16 * t * C::ROWB);
         const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t], o[dt], 0, 0, 0);
       }
@@ -335,20 +345,21 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     exp_pack(s_cur, pb);
     pv(VSLOT0 + PAR * C::BLKB, pb);
     mx = blockmax(s_nxt);
-    // Interleave: score MFMAs with operand reads kept 4 ahead and the exponentials; then
-    // the PV MFMAs with their transposing reads kept two MFMAs ahead and the next max.
+    // Interleave: score MFMAs with their operand reads kept 4 ahead and the exponentials;
+    // the slots of the last four score MFMAs already issue the first 8 transposing V reads,
+    // which then run 4 MFMAs ahead of the PV MFMAs, interleaved with the next max.
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 2 * C::KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i + 4 < 2 * C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 4 * C::DT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + 2 < 4 * C::DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i + 4 < 4 * C::DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -482,7 +493,8 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
 
   // ---- epilogue: normalise, bf16, restage per wave, store rows into their slabs ----------
   const float inv = 1.0f / sum_with_partner32(l_run);
-  char* stage = smem + w * 32 * C::ROWB;  // wave-private [32][D] (buffers are free after the loop)
+  // wave-private [32][D] restage area in the K slots (free after the loop)
+  char* stage = (w < 2 ? lds_k0 : lds_k1) + (w & 1) * 32 * C::ROWB;
   {
     const int n = lane & 31;
     const int sw = swz<D>(n);
