@@ -35,6 +35,7 @@ __all__ = [
     "xstage_a2a_scatter",
     "xstage_attn_a2a_unfused",
     "xstage_attn_a2a_plan",
+    "xstage_attn_a2a_schedule",
     "xstage_attn_a2a_fwd_traced",
     "xstage_burst_gap_run",
     "xstage_wallclock_hz",
@@ -157,6 +158,17 @@ def xstage_attn_a2a_plan(B: int, S: int, H_local: int, D: int):
     _check(lib().xstage_attn_a2a_plan(int(B), int(S), int(H_local), int(D), ctypes.byref(nwg), ctypes.byref(nsp)),
            "xstage_attn_a2a_plan")
     return nwg.value, nsp.value
+
+
+def xstage_attn_a2a_schedule(B: int, S: int, H_local: int, D: int):
+    """Per-workgroup (tile, split, j0, j1) of the attention launch for this shape on the
+    current device, as four lists (key blocks of 64 in [j0, j1))."""
+    nwg, _ = xstage_attn_a2a_plan(B, S, H_local, D)
+    arrs = [(ctypes.c_int * max(nwg, 1))() for _ in range(4)]
+    n = ctypes.c_int(0)
+    _check(lib().xstage_attn_a2a_schedule(int(B), int(S), int(H_local), int(D), nwg, *arrs, ctypes.byref(n)),
+           "xstage_attn_a2a_schedule")
+    return tuple(list(a)[: n.value] for a in arrs)
 
 
 def xstage_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, stream=None) -> None:

@@ -9,6 +9,7 @@ namespace xstage {
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
                     int P, float scale, hipStream_t stream, int mode = 0, unsigned long long* stamps = nullptr);
 int attn_workgroups(int B, int S, int H, int D, int* n_split);
+int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, int* j0, int* j1);
 int launch_scatter(const void* in, const SlabTable& slabs, int B, int S, int H, int D, int P, hipStream_t stream);
 int launch_burst_gap(const xstage_bg_params_t& p, hipStream_t stream);
 
@@ -86,6 +87,15 @@ int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, in
   if (st != XSTAGE_OK) return st;
   *n_workgroups = attn_workgroups(B, S, H_local, D, n_split);
   return XSTAGE_OK;
+}
+
+int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, int cap, int* tile, int* split, int* j0, int* j1,
+                             int* n_workgroups) {
+  if (n_workgroups == nullptr || cap < 0 || (cap > 0 && (!tile || !split || !j0 || !j1))) return XSTAGE_ERR_INVALID;
+  const int st = check_shape(B, S, H_local, D, 1);
+  if (st != XSTAGE_OK) return st;
+  *n_workgroups = attn_schedule(B, S, H_local, D, cap, tile, split, j0, j1);
+  return *n_workgroups > cap ? XSTAGE_ERR_INVALID : XSTAGE_OK;
 }
 
 int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,

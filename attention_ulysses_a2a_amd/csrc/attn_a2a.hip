@@ -21,6 +21,7 @@
 //   * epilogue: normalise, round to bf16, restage the tile through LDS and write each row's
 //     16-byte chunks straight into the slab owning that sequence row.  The stores are not
 //     waited on.
+#include <algorithm>
 #include <math.h>
 
 #include "common.hpp"
@@ -64,7 +65,8 @@ struct AttnArgs {
   int n_mtiles;
   int n_units;       // workgroups: (b, h, m-tile) tiles x key splits
   int n_split;       // key-range splits per tile (1: no merge)
-  int kvb_per_split; // 64-key blocks per split
+  int kvb_per_split; // 64-key blocks per split (uniform splits)
+  int use_table;     // 1: per-workgroup (tile, split, key range) from the unit table
   float c;           // |scale| * log2(e): scores are turned into base-2 logits
   uint32_t qflip;    // 0x80008000 for a negative scale: Q is negated on load
   f32x4* partial;    // split partials: [tile][split][wave][chunk][64 lanes] (n_split > 1)
@@ -93,7 +95,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, const UnitTable tab) {
   // The body names device-only types (the buffer resource), which the host pass of a
   // template cannot instantiate; the host pass only needs the launch signature.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -128,16 +130,31 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
     }
   };
 
-  // XCD-aware unit order: workgroup i runs on XCD i % 8; give each XCD a contiguous range
-  // of (b, h, m-tile) units so that one head's K/V stays in one XCD's L2.
-  int L;
+  const int nkv = (a.S + C::BN - 1) / C::BN;
+  // This workgroup's tile, split and key-block range [j0, j1).  One-round launches take
+  // them from the unit table (kernel arguments: one scalar load, issued with the others).
+  // Otherwise the order is XCD-aware: workgroup i runs on XCD i % 8; each XCD gets a
+  // contiguous range of (b, h, m-tile) units so that one head's K/V stays in one XCD's L2,
+  // and the splits are uniform.
+  int tile, split, j0, j1;
   {
-    const int i = blockIdx.x, n = a.n_units;
-    const int q8 = n >> 3, r8 = n & 7, xcd = i & 7, slot = i >> 3;
-    L = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
+    const int i = blockIdx.x;
+    const uint32_t e = tab.e[i < kUnitTableCap ? i : 0];
+    if (a.use_table) {
+      tile = e & 1023;
+      split = (e >> 10) & 15;
+      j0 = (e >> 14) & 511;
+      j1 = e >> 23;
+    } else {
+      const int n = a.n_units;
+      const int q8 = n >> 3, r8 = n & 7, xcd = i & 7, slot = i >> 3;
+      const int L = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
+      tile = L / a.n_split;
+      split = L - tile * a.n_split;
+      j0 = split * a.kvb_per_split;
+      j1 = min(j0 + a.kvb_per_split, nkv);
+    }
   }
-  const int tile = L / a.n_split;
-  const int split = L - tile * a.n_split;
   const int mt = tile % a.n_mtiles;
   const int bh = tile / a.n_mtiles;
   const int h = bh % a.H;
@@ -247,7 +264,6 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   // Keys past S exist only in the very last block (`tail`): their scores become -inf, so
   // they drop out of the max and get weight exp2(-inf) = 0 (c > 0 always, see above).
   constexpr float kLazy = 8.0f;
-  const int nkv = (S + C::BN - 1) / C::BN;
   auto key_of = [&](int n0, int t, int r) { return n0 + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3); };
   auto mask_tail = [&](f32x16* st, int n0) {
 #pragma unroll
@@ -322,8 +338,6 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a) {
   // loads and meets the other waves at the barrier.  Slot parity alternates with j - j0;
   // the loop is unrolled by two so it is static.  Rows past S (zeros) are only in the last
   // block, handled after the loop: there the max is recomputed with those keys at -inf.
-  const int j0 = split * a.kvb_per_split;
-  const int j1 = min(j0 + a.kvb_per_split, nkv);
   f32x16 s_a[2], s_b[2];
   bf16x8 pb[4];
   float mx;
@@ -597,12 +611,16 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.partial = static_cast<f32x4*>(plan.partial);
   a.counters = plan.counters;
   a.stamps = stamps;
+  static const UnitTable kNoTable = {};
+  const UnitTable* tab = plan.n_split > 1 ? unit_table(a.n_units / plan.n_split, (S + 63) / 64, plan.n_split) : nullptr;
+  a.use_table = tab != nullptr;
+  const UnitTable& t = tab ? *tab : kNoTable;
   const dim3 grid(a.n_units), block(AttnCfg<D>::THREADS);
   switch (mode) {
-    case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced>), grid, block, 0, stream, a); break;
-    case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled>), grid, block, 0, stream, a); break;
-    case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun>), grid, block, 0, stream, a); break;
+    case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced>), grid, block, 0, stream, a, t); break;
+    case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled>), grid, block, 0, stream, a, t); break;
+    case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore>), grid, block, 0, stream, a, t); break;
+    default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun>), grid, block, 0, stream, a, t); break;
   }
   return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
 }
@@ -616,6 +634,32 @@ int attn_workgroups(int B, int S, int H, int D, int* n_split) {
   const SplitPlan plan = choose_split(n_tiles, (S + 63) / 64, D, partial_bytes_per_unit(D));
   if (n_split) *n_split = plan.n_split;
   return n_tiles * plan.n_split;
+}
+
+int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, int* j0, int* j1) {
+  const int n_tiles = B * H * ((S + 127) / 128);
+  const int nkv = (S + 63) / 64;
+  const SplitPlan plan = choose_split(n_tiles, nkv, D, partial_bytes_per_unit(D));
+  const int n = n_tiles * plan.n_split;
+  if (n > cap) return n;
+  const UnitTable* tab = plan.n_split > 1 ? unit_table(n_tiles, nkv, plan.n_split) : nullptr;
+  for (int i = 0; i < n; ++i) {
+    if (tab) {
+      const uint32_t e = tab->e[i];
+      tile[i] = e & 1023;
+      split[i] = (e >> 10) & 15;
+      j0[i] = (e >> 14) & 511;
+      j1[i] = e >> 23;
+    } else {  // the kernel's XCD-contiguous order with uniform splits
+      const int q8 = n / 8, r8 = n % 8, x = i % 8, slot = i / 8;
+      const int L = x < r8 ? x * (q8 + 1) + slot : r8 * (q8 + 1) + (x - r8) * q8 + slot;
+      tile[i] = L / plan.n_split;
+      split[i] = L % plan.n_split;
+      j0[i] = split[i] * plan.kvb_per_split;
+      j1[i] = std::min(j0[i] + plan.kvb_per_split, nkv);
+    }
+  }
+  return n;
 }
 
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,

@@ -20,6 +20,34 @@ struct SplitPlan {
 // co-resident workgroups (two per compute unit) and of the merge of split tiles.
 SplitPlan choose_split(int n_tiles, int nkv, int D, size_t partial_bytes_per_unit);
 
+// Per-workgroup work of a launch whose workgroups all fit on the device at once.  Workgroups
+// are dispatched in index order, round-robin over the 8 XCDs (i % 8), and each XCD fills
+// every CU once before it places a second workgroup on any: with c CUs per XCD and n
+// workgroups on it, slots (i / 8) 0 .. n-c-1 share their CU with slots c .. n-1, and the
+// slots in between have a CU to themselves.  Two workgroups on one CU do not progress
+// alike: the older one (lower slot) keeps most of the issue slots.  Measured per-block
+// rates relative to a lone workgroup (MI355X, D = 128): older sharer 0.864, younger sharer
+// 0.58.  The table assigns every workgroup a (tile, split, key-block range) so that each
+// tile mixes these classes and each split's range is proportional to its rate: the splits
+// of a tile then finish together and no tile waits on an all-younger-sharer group.  Only
+// speed depends on this; any table that partitions every tile's keys is correct.
+constexpr int kUnitTableCap = 512;
+struct UnitTable {
+  uint32_t e[kUnitTableCap];  // tile | split << 10 | j0 << 14 | j1 << 23
+};
+constexpr uint32_t unit_entry(int tile, int split, int j0, int j1) {
+  return (uint32_t)tile | (uint32_t)split << 10 | (uint32_t)j0 << 14 | (uint32_t)j1 << 23;
+}
+
+// Table for n_tiles tiles of n_split splits over nkv key blocks on `cus` compute units, or
+// false when the launch is outside its scope (more workgroups than fit at once, no more
+// than one per CU, more than kUnitTableCap workgroups, nkv > 511, fewer than 2 blocks per
+// split, CU count not a multiple of 8).
+bool build_unit_table(int n_tiles, int nkv, int n_split, int cus, UnitTable* table);
+
+// Cached build_unit_table for the current device (nullptr when out of scope).
+const UnitTable* unit_table(int n_tiles, int nkv, int n_split);
+
 // Returns buffers of at least `partial_bytes` and `n_counters` zeroed counters owned by the
 // library for (current device, stream).  Grows them on demand: growing synchronizes
 // `stream` first (the old buffers may still be read by earlier launches on it).

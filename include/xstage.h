@@ -96,6 +96,18 @@ int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* w
  * sizes the stamps of xstage_attn_a2a_fwd_traced. */
 int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_split);
 
+/* The work decomposition xstage_attn_a2a_fwd uses for this shape on the current device
+ * (256 CUs assumed when no device is present): for each of the *n_workgroups workgroups,
+ * the tile it computes (index over (b, h, 128-row m-tile), m-tile fastest), its split
+ * index within the tile (the merge order) and its half-open range [j0, j1) of 64-key
+ * blocks.  The ranges of a tile's splits partition [0, ceil(S / 64)) in split order.
+ * Launches whose workgroups fit on the device at once (more than one per CU) use ranges
+ * sized to each workgroup's CU placement; others use equal ranges.  Host only; the four
+ * arrays hold at least `cap` ints (caller-owned); cap < *n_workgroups writes nothing and
+ * returns XSTAGE_ERR_INVALID with *n_workgroups set. */
+int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, int cap, int* tile, int* split,
+                             int* j0, int* j1, int* n_workgroups);
+
 /* Instrumented xstage_attn_a2a_fwd for the per-tile store-span study ("Results",
  * FlashAttention-A2A: the measured overhead against the completion-coupled counterfactual;
  * "Contributions", X-Stage item: neither a fully blocking nor an unbounded asynchronous

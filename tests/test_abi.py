@@ -7,6 +7,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import attention_ulysses_a2a_amd as xs
@@ -46,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -161,6 +162,58 @@ def test_plan_counts_workgroups(L):
     assert L.xstage_attn_a2a_plan(1, 256, 2, 80, _lib.ctypes.byref(n), None) == UNSUPPORTED
     assert L.xstage_attn_a2a_plan(0, 256, 2, 64, _lib.ctypes.byref(n), None) == INVALID
     assert L.xstage_attn_a2a_plan(1, 256, 2, 64, None, None) == INVALID
+
+
+SCHEDULE_SHAPES = [(1, 256, 2, 64), (1, 4608, 3, 128), (1, 4608, 3, 64), (2, 4608, 3, 128), (1, 9216, 3, 128),
+                   (1, 2304, 3, 128), (1, 16896, 3, 128), (1, 32760, 5, 128), (2, 1000, 2, 128), (1, 1, 1, 64)]
+
+
+@pytest.mark.parametrize("B,S,H,D", SCHEDULE_SHAPES)
+def test_schedule_partitions_every_tile(L, B, S, H, D):
+    """Host-only: every tile's splits cover its key blocks [0, ceil(S/64)) exactly once, in
+    split order, and every workgroup has its own (tile, split)."""
+    tile, split, j0, j1 = (np.array(a) for a in xs.xstage_attn_a2a_schedule(B, S, H, D))
+    nwg, nsp = xs.xstage_attn_a2a_plan(B, S, H, D)
+    n_tiles, nkv = B * H * ((S + 127) // 128), (S + 63) // 64
+    assert len(tile) == nwg == n_tiles * nsp
+    assert len(set(zip(tile.tolist(), split.tolist()))) == nwg
+    for t in range(n_tiles):
+        idx = np.where(tile == t)[0]
+        o = idx[np.argsort(split[idx])]
+        assert split[o].tolist() == list(range(nsp))
+        assert j0[o[0]] == 0 and j1[o[-1]] == nkv
+        assert np.array_equal(j1[o[:-1]], j0[o[1:]])
+        assert np.all(j1[o] > j0[o])
+
+
+def test_schedule_mixes_placements_in_one_round(L):
+    """FLUX-1024 share: 432 workgroups on 256 CUs (8 XCDs of 32) run in one round; workgroup
+    i sits at slot i // 8 of XCD i % 8, slots 0..21 share a CU with slots 32..53 (the
+    younger, slower partner) and 22..31 run alone.  No tile may be all younger partners, and
+    a younger partner never gets more keys than an older partner or a lone workgroup of
+    its tile."""
+    tile, split, j0, j1 = (np.array(a) for a in xs.xstage_attn_a2a_schedule(1, 4608, 3, 128))
+    blocks = j1 - j0
+    slot = np.arange(len(tile)) // 8
+    young = slot >= 32
+    assert len(set(blocks.tolist())) > 1       # ranges follow the placement
+    for t in range(tile.max() + 1):
+        idx = np.where(tile == t)[0]
+        assert not young[idx].all()
+        if young[idx].any() and (~young[idx]).any():
+            assert blocks[idx][young[idx]].max() <= blocks[idx][~young[idx]].min()
+    # multi-round launches keep equal ranges (the last split may be shorter)
+    tile, split, j0, j1 = (np.array(a) for a in xs.xstage_attn_a2a_schedule(1, 16896, 3, 128))
+    assert len(set((j1 - j0)[j1 < (16896 + 63) // 64].tolist())) == 1
+
+
+def test_schedule_rejects(L):
+    n = _lib.ctypes.c_int(0)
+    buf = (_lib.ctypes.c_int * 4)()
+    assert L.xstage_attn_a2a_schedule(1, 4608, 3, 128, 4, buf, buf, buf, buf, _lib.ctypes.byref(n)) == INVALID
+    assert n.value == xs.xstage_attn_a2a_plan(1, 4608, 3, 128)[0]
+    assert L.xstage_attn_a2a_schedule(1, 256, 2, 64, 0, None, None, None, None, None) == INVALID
+    assert L.xstage_attn_a2a_schedule(1, 256, 2, 80, 0, None, None, None, None, _lib.ctypes.byref(n)) == UNSUPPORTED
 
 
 STAMPS = 0x50_0000_0000

@@ -154,6 +154,35 @@ def test_extra_shapes(B, S, H, D, P, scale):
     assert np.array_equal(gp.slabs_host(), oracle.ulysses_scatter(pv, P))
 
 
+# Shapes whose workgroups all fit on the device at once and so take key ranges sized to
+# their CU placement (unequal ranges; 4 splits at D = 64, 2 splits at B = 2 and S = 9216).
+TABLE_SHAPES = [
+    # (B, S, H, D, P, full oracle)
+    (1, 4608, 3, 64, 8, True),
+    (2, 4608, 3, 128, 8, True),
+    (1, 9216, 3, 128, 8, False),
+]
+
+
+@pytest.mark.parametrize("B,S,H,D,P,full", TABLE_SHAPES)
+def test_placement_sized_key_ranges(B, S, H, D, P, full):
+    tile, split, j0, j1 = (np.array(a) for a in xs.xstage_attn_a2a_schedule(B, S, H, D))
+    assert len(set((j1 - j0).tolist())) > 1  # this shape takes the placement-sized ranges
+    w = Workload("table", B, S, H, D, P, seed=23 + S + D + B)
+    log(f"placement-sized key ranges: B={B} S={S} H={H} D={D} P={P} workgroups={len(tile)}")
+    qb, kb, vb = make_inputs(w)
+    g = run_fused(w, qb, kb, vb, w.scale)
+    assert g.guards_intact()
+    slabs = g.slabs_host()
+    assert not np.any(slabs == NAN_BF16)
+    compare_values(f"table-{B}x{S}x{H}x{D}", slabs, qb, kb, vb, w.scale, None if full else sample_rows(S, S // P))
+    assert np.array_equal(slabs, run_unfused(w, qb, kb, vb, w.scale).slabs_host())
+    pq, pk, pv = make_placement_probe(B, S, H, D, w.scale)
+    gp = run_fused(w, pq, pk, pv, w.scale)
+    assert gp.guards_intact()
+    assert np.array_equal(gp.slabs_host(), oracle.ulysses_scatter(pv, P))
+
+
 def test_attn_fwd_contiguous_matches_oracle():
     w = workload("tiny")
     qb, kb, vb = make_inputs(w)
