@@ -34,6 +34,8 @@ __all__ = [
     "xstage_attn_fwd",
     "xstage_a2a_scatter",
     "xstage_attn_a2a_unfused",
+    "xstage_attn_a2a_fwd_strided",
+    "xstage_ulysses_attn_fwd",
     "xstage_attn_a2a_plan",
     "xstage_attn_a2a_schedule",
     "xstage_attn_a2a_fwd_traced",
@@ -84,6 +86,78 @@ def _slab_ptrs(out_slabs):
     for i, s in enumerate(slabs):
         _dev_tensor(s, f"out_slabs[{i}]")
     return [s.data_ptr() for s in slabs], len(slabs)
+
+
+def _shards(x, name):
+    """Device pointers and the common [B, S/P, H, D] shape of P shards, given as a list of
+    tensors or one [P, B, S/P, H, D] tensor."""
+    import torch
+
+    if isinstance(x, torch.Tensor):
+        _dev_tensor(x, name)
+        if x.dim() != 5:
+            raise ValueError(f"{name} must be [P, B, S/P, H, D]")
+        return [x[p].data_ptr() for p in range(x.shape[0])], tuple(int(d) for d in x.shape[1:])
+    xs = list(x)
+    if not xs:
+        raise ValueError(f"{name} is empty")
+    for i, t in enumerate(xs):
+        _dev_tensor(t, f"{name}[{i}]")
+        if t.dim() != 4 or t.shape != xs[0].shape:
+            raise ValueError(f"{name} must be P tensors of one [B, S/P, H, D] shape")
+    return [t.data_ptr() for t in xs], tuple(int(d) for d in xs[0].shape)
+
+
+def _strided_call(q, k, v, out_dst, h_dst0, scale, stream):
+    B, S, H, D = _qkv(q, k, v)
+    ptrs, shp = _shards(out_dst, "out_dst")
+    P = len(ptrs)
+    if shp[0] != B or shp[1] * P != S or shp[3] != D:
+        raise ValueError("out_dst must be P buffers of [B, S/P, H_dst, D]")
+    arr, keep = ptr_array(ptrs)
+    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, shp[2], int(h_dst0), _scale(scale, D),
+            _stream_of(q, stream)), keep
+
+
+def _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream):
+    qp, shp = _shards(q_src, "q_src")
+    kp, kshp = _shards(k_src, "k_src")
+    vp, vshp = _shards(v_src, "v_src")
+    op, oshp = _shards(out_dst, "out_dst")
+    P = len(qp)
+    if not (len(kp) == len(vp) == len(op) == P and kshp == vshp == oshp == shp):
+        raise ValueError("q_src, k_src, v_src, out_dst must be P shards of one [B, S/P, H, D] shape")
+    B, sp, H, D = shp
+    arrs = [ptr_array(x) for x in (qp, kp, vp, op)]
+    t0 = q_src if not isinstance(q_src, (list, tuple)) else q_src[0]
+    call = (arrs[0][0], arrs[1][0], arrs[2][0], arrs[3][0], B, sp * P, H, int(H_local), int(h0), D, P,
+            _scale(scale, D), _stream_of(t0, stream))
+    return call, [a[1] for a in arrs], t0.device
+
+
+def xstage_attn_a2a_fwd_strided(q, k, v, out_dst, h_dst0, scale=None, stream=None) -> None:
+    """Fused call writing head columns [h_dst0, h_dst0 + H_local) of full-head receive
+    buffers out_dst (P x [B, S/P, H_dst, D]); see include/xstage.h."""
+    import torch
+
+    call, keep = _strided_call(q, k, v, out_dst, h_dst0, scale, stream)
+    with torch.cuda.device(q.device):
+        st = lib().xstage_attn_a2a_fwd_strided(*call)
+    del keep
+    _check(st, "xstage_attn_a2a_fwd_strided")
+
+
+def xstage_ulysses_attn_fwd(q_src, k_src, v_src, out_dst, H_local, h0, scale=None, stream=None) -> None:
+    """One rank's Ulysses attention layer: heads [h0, h0 + H_local) read from the P sequence
+    shards (P x [B, S/P, H, D] each) and written into the P receive buffers; see
+    include/xstage.h."""
+    import torch
+
+    call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
+    with torch.cuda.device(dev):
+        st = lib().xstage_ulysses_attn_fwd(*call)
+    del keep
+    _check(st, "xstage_ulysses_attn_fwd")
 
 
 def _qkv(q, k, v):
@@ -242,7 +316,9 @@ def bind(name: str, *args, **kwargs) -> _Bound:
     bound buffers are kept alive by the callable; the stream is fixed at bind time (the
     current stream of the tensors' device unless ``stream`` is given), and the calls must be
     made with that device current.  Supported: xstage_attn_a2a_fwd, xstage_attn_fwd,
-    xstage_a2a_scatter, xstage_attn_a2a_unfused, with the same arguments as the functions.
+    xstage_a2a_scatter, xstage_attn_a2a_unfused, xstage_attn_a2a_fwd_traced,
+    xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd, with the same arguments as the
+    functions.
     """
     import torch
 
@@ -291,6 +367,16 @@ def bind(name: str, *args, **kwargs) -> _Bound:
         call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), int(mode),
                 stamps.data_ptr(), _stream_of(q, stream))
         refs, dev = (q, k, v, out_slabs, stamps, keep), q.device
+    elif name == "xstage_attn_a2a_fwd_strided":
+        q, k, v, out_dst, h_dst0 = args[:5]
+        scale, stream = kwargs.get("scale", args[5] if len(args) > 5 else None), kwargs.get("stream")
+        call, keep = _strided_call(q, k, v, out_dst, h_dst0, scale, stream)
+        refs, dev = (q, k, v, out_dst, keep), q.device
+    elif name == "xstage_ulysses_attn_fwd":
+        q_src, k_src, v_src, out_dst, H_local, h0 = args[:6]
+        scale, stream = kwargs.get("scale", args[6] if len(args) > 6 else None), kwargs.get("stream")
+        call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
+        refs = (q_src, k_src, v_src, out_dst, keep)
     else:
         raise ValueError(f"bind: unsupported entry point {name!r}")
     if torch.cuda.current_device() != dev.index:

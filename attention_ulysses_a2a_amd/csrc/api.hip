@@ -2,12 +2,15 @@
 // and contracts: include/xstage.h.
 #include <math.h>
 
+#include <cmath>
+
 #include "common.hpp"
 #include "validate.hpp"
 
 namespace xstage {
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
-                    int P, float scale, hipStream_t stream, int mode = 0, unsigned long long* stamps = nullptr);
+                    int P, float scale, hipStream_t stream, int mode = 0, unsigned long long* stamps = nullptr,
+                    const Layout* layout = nullptr);
 int attn_workgroups(int B, int S, int H, int D, int* n_split);
 int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, int* j0, int* j1);
 int launch_scatter(const void* in, const SlabTable& slabs, int B, int S, int H, int D, int P, hipStream_t stream);
@@ -79,6 +82,59 @@ int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* w
   st = launch_attn_any(q, k, v, make_table(one, 1), B, S, H_local, D, 1, scale, s);
   if (st != XSTAGE_OK) return st;
   return launch_scatter(workspace, make_table(out_slabs, P), B, S, H_local, D, P, s);
+}
+
+int xstage_attn_a2a_fwd_strided(const void* q, const void* k, const void* v, void* const* out_dst, int B, int S,
+                                int H_local, int D, int P, int H_dst, int h_dst0, float scale, void* stream) {
+  int st = check_shape(B, S, H_local, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (H_dst < H_local || h_dst0 < 0 || h_dst0 > H_dst - H_local) return XSTAGE_ERR_INVALID;
+  st = check_shape(B, S, H_dst, D, P);  // destination element offsets stay 32-bit
+  if (st != XSTAGE_OK) return st;
+  st = check_qkv(q, k, v, scale);
+  if (st != XSTAGE_OK) return st;
+  const unsigned long long tb = tensor_bytes(B, S, H_local, D);
+  const Range others[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  st = check_slabs(out_dst, P, tensor_bytes(B, S, H_dst, D) / (unsigned long long)P, others, 3);
+  if (st != XSTAGE_OK) return st;
+  Layout lay;
+  lay.dst_heads = H_dst;
+  lay.dst_head0 = h_dst0;
+  return launch_attn_any(q, k, v, make_table(out_dst, P), B, S, H_local, D, P, scale, static_cast<hipStream_t>(stream),
+                         0, nullptr, &lay);
+}
+
+int xstage_ulysses_attn_fwd(const void* const* q_src, const void* const* k_src, const void* const* v_src,
+                            void* const* out_dst, int B, int S, int H, int H_local, int h0, int D, int P, float scale,
+                            void* stream) {
+  int st = check_shape(B, S, H, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (H_local <= 0 || H_local > H || h0 < 0 || h0 > H - H_local) return XSTAGE_ERR_INVALID;
+  if (P > kMaxSrc) return XSTAGE_ERR_UNSUPPORTED;
+  if (q_src == nullptr || k_src == nullptr || v_src == nullptr || !std::isfinite(scale)) return XSTAGE_ERR_INVALID;
+  const unsigned long long shard = tensor_bytes(B, S, H, D) / (unsigned long long)P;
+  Range src_ranges[3 * kMaxSrc];
+  SrcTable t = {};
+  for (int p = 0; p < P; ++p) {
+    const void* ptrs[3] = {q_src[p], k_src[p], v_src[p]};
+    for (int j = 0; j < 3; ++j) {
+      if (ptrs[j] == nullptr || !aligned16(ptrs[j])) return XSTAGE_ERR_INVALID;
+      src_ranges[3 * p + j] = range_of(ptrs[j], shard);
+    }
+    t.q[p] = static_cast<const uint16_t*>(q_src[p]);
+    t.k[p] = static_cast<const uint16_t*>(k_src[p]);
+    t.v[p] = static_cast<const uint16_t*>(v_src[p]);
+  }
+  st = check_slabs(out_dst, P, shard, src_ranges, 3 * P);
+  if (st != XSTAGE_OK) return st;
+  Layout lay;
+  lay.src = &t;
+  lay.src_heads = H;
+  lay.src_head0 = h0;
+  lay.dst_heads = H;
+  lay.dst_head0 = h0;
+  return launch_attn_any(q_src[0], k_src[0], v_src[0], make_table(out_dst, P), B, S, H_local, D, P, scale,
+                         static_cast<hipStream_t>(stream), 0, nullptr, &lay);
 }
 
 int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_split) {

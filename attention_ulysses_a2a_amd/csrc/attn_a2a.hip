@@ -67,6 +67,11 @@ struct AttnArgs {
   int n_split;       // key-range splits per tile (1: no merge)
   int kvb_per_split; // 64-key blocks per split (uniform splits)
   int use_table;     // 1: per-workgroup (tile, split, key range) from the unit table
+  // Input layout: n_src sequence shards of src_rows rows each (n_src = 1: q, k, v above),
+  // rows of src_hs heads, this call's heads starting at src_h0.  Output layout: P slabs of
+  // S_P rows, rows of dst_hs heads, this call's heads written from column dst_h0 on.
+  int src_rows, src_hs, src_h0;
+  int dst_hs, dst_h0;
   float c;           // |scale| * log2(e): scores are turned into base-2 logits
   uint32_t qflip;    // 0x80008000 for a negative scale: Q is negated on load
   f32x4* partial;    // split partials: [tile][split][wave][chunk][64 lanes] (n_split > 1)
@@ -89,13 +94,19 @@ __device__ __forceinline__ uint16_t* uniform_ptr(uint16_t* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return reinterpret_cast<uint16_t*>(((uint64_t)hi << 32) | lo);
 }
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  return uniform_ptr(const_cast<uint16_t*>(p));
+}
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, const UnitTable tab) {
+struct NoSrc {};
+
+template <int D, int MODE, bool SRC>
+__global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, const UnitTable tab,
+                                                          const std::conditional_t<SRC, SrcTable, NoSrc> src) {
   // The body names device-only types (the buffer resource), which the host pass of a
   // template cannot instantiate; the host pass only needs the launch signature.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -161,11 +172,9 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   const int b = bh / a.H;
   const int m0 = mt * C::BM;
   const int S = a.S;
-  const uint32_t rs = (uint32_t)a.H * D;  // elements between consecutive rows of one head
-  const uint32_t head0 = ((uint32_t)b * S * a.H + h) * D;
-  const uint16_t* qb = a.q + head0;
-  const uint16_t* kb = a.k + head0;
-  const uint16_t* vb = a.v + head0;
+  const uint32_t rs = (uint32_t)a.src_hs * D;  // elements between consecutive rows of one head
+  // offset of (b, first row of a shard, this head) within a shard
+  const uint32_t head0 = ((uint32_t)b * a.src_rows * a.src_hs + a.src_h0 + h) * D;
 
   // Q fragment (B operand of the score MFMA): lane holds query (lane & 31), d = 16ks + 8*hl + 0..7
   bf16x8 qf[C::KS];
@@ -174,7 +183,18 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < S) x = *reinterpret_cast<const u32x4*>(qb + (uint32_t)qrow * rs + ks * 16 + hl * 8);
+      if (qrow < S) {
+        const uint16_t* qb;
+        int r = qrow;
+        if constexpr (SRC) {
+          const int p = qrow / a.src_rows;
+          r = qrow - p * a.src_rows;
+          qb = src.q[p] + head0;
+        } else {
+          qb = a.q + head0;
+        }
+        x = *reinterpret_cast<const u32x4*>(qb + (uint32_t)r * rs + ks * 16 + hl * 8);
+      }
       x ^= a.qflip;
       qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
@@ -183,13 +203,23 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   // K/V blocks go from global memory straight into LDS (buffer_load_dwordx4 ... lds: no
   // registers).  One instruction of wave w fills the 1 KiB LDS segment (i*4 + w) of a
   // block, lane by lane, so each lane fetches the global chunk that belongs at its LDS slot
-  // under the swizzle.  The buffer resource spans the S rows of this (b, h): the block
-  // offset is a scalar, each lane's offset within a block is fixed, and rows past the end
-  // of the sequence read as zeros (hardware range check) — no clamping, no branches.
+  // under the swizzle.  The buffer resource spans the S rows of this (b, h); a lane's
+  // offset is its fixed offset within a block plus the block's, all in the per-lane
+  // offset (the scalar offset stays 0, so the range check sees the whole offset): rows
+  // past the end of the sequence read as zeros — no clamping, no branches.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int head_bytes = (int)((uint32_t)S * rs * 2u);
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, head_bytes, 0x00020000);
+  const int head_bytes = (int)((uint32_t)a.src_rows * rs * 2u);  // one shard's rows of this head
+  auto make_rsrc = [&](const uint16_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + head0), (short)0, head_bytes, 0x00020000);
+  };
+  // One shard (SRC = false): the buffer resources are fixed.  Shards (SRC = true): they are
+  // built per block from the shard pointer (kernel arguments, scalar loads); the tables
+  // index 0 = K, 1 = V.
+  __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+  if constexpr (!SRC) {
+    krsrc = make_rsrc(a.k);
+    vrsrc = make_rsrc(a.v);
+  }
   uint32_t ld_voff[C::NLD];  // byte offset of this lane's chunk from the block's first key
 #pragma unroll
   for (int i = 0; i < C::NLD; ++i) {
@@ -198,12 +228,36 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
     ld_voff[i] = ((uint32_t)row * rs + (uint32_t)((pc ^ swz<D>(row)) * 8)) * 2u;
   }
   auto dload = [&](const __amdgpu_buffer_rsrc_t& rsrc, int slot_byte, int n0) {
-    const uint32_t soff = (uint32_t)n0 * rs * 2u;
+    if constexpr (!SRC) {
+      const uint32_t boff = (uint32_t)n0 * rs * 2u;
 #pragma unroll
-    for (int i = 0; i < C::NLD; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16, ld_voff[i],
-          soff, 0, 0);
+      for (int i = 0; i < C::NLD; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
+            ld_voff[i] + boff, 0, 0, 0);
+    } else {
+      // Rows n0 .. n0+63 come from shards p0 .. p1 (one, unless the block straddles a shard
+      // boundary).  The last shard also takes the rows past S, which lie beyond its range
+      // and read as zeros.  A lane loads from exactly one shard, so every LDS chunk is
+      // written once.
+      const uint16_t* const* tbl = slot_byte < 2 * C::BLKB ? src.k : src.v;
+      const int last = min(n0 + C::BN, S) - 1;
+      const int p0 = n0 / a.src_rows, p1 = last / a.src_rows;
+      for (int p = p0; p <= p1; ++p) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(tbl[p]));
+        const int lo = p * a.src_rows - n0;                        // first block row in shard p
+        const int hi = p == p1 ? C::BN : (p + 1) * a.src_rows - n0;  // one past its last
+        const uint32_t boff = (uint32_t)(n0 - p * a.src_rows) * rs * 2u;
+#pragma unroll
+        for (int i = 0; i < C::NLD; ++i) {
+          const int row = ((i * 4 + w) * 64 + lane) / C::CH;
+          if (p0 == p1 || (row >= lo && row < hi))
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
+                ld_voff[i] + boff, 0, 0, 0);
+        }
+      }
+    }
   };
 
   // LDS slots: K at byte 0 and BLKB, V at 2*BLKB and 3*BLKB.  Every per-lane read address
@@ -551,7 +605,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       const int s_row = row0 + row;
       const bool hi = s_row >= p_hi * a.S_P;
       const int r = s_row - (hi ? p_hi : p_lo) * a.S_P;
-      const uint32_t off = (((uint32_t)b * a.S_P + r) * a.H + h) * D + ch * 8;
+      const uint32_t off = (((uint32_t)b * a.S_P + r) * a.dst_hs + a.dst_h0 + h) * D + ch * 8;
       dst[i] = (g_u32x4*)((hi ? base_hi : base_lo) + off);
     }
     if (full) {
@@ -572,7 +626,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       if (s_row < S) {
         const int p = s_row / a.S_P;
         const int r = s_row - p * a.S_P;
-        const uint32_t off = (((uint32_t)b * a.S_P + r) * a.H + h) * D + ch * 8;
+        const uint32_t off = (((uint32_t)b * a.S_P + r) * a.dst_hs + a.dst_h0 + h) * D + ch * 8;
         *reinterpret_cast<u32x4*>(a.slabs.p[p] + off) = val;
       }
     }
@@ -592,7 +646,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
 template <int D>
 static int launch_attn(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H,
                        int P, float scale, const SplitPlan& plan, int mode, unsigned long long* stamps,
-                       hipStream_t stream) {
+                       const Layout& lay, hipStream_t stream) {
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -611,16 +665,27 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.partial = static_cast<f32x4*>(plan.partial);
   a.counters = plan.counters;
   a.stamps = stamps;
+  a.src_rows = lay.src ? S / P : S;
+  a.src_hs = lay.src_heads > 0 ? lay.src_heads : H;
+  a.src_h0 = lay.src_head0;
+  a.dst_hs = lay.dst_heads > 0 ? lay.dst_heads : H;
+  a.dst_h0 = lay.dst_head0;
   static const UnitTable kNoTable = {};
   const UnitTable* tab = plan.n_split > 1 ? unit_table(a.n_units / plan.n_split, (S + 63) / 64, plan.n_split) : nullptr;
   a.use_table = tab != nullptr;
   const UnitTable& t = tab ? *tab : kNoTable;
   const dim3 grid(a.n_units), block(AttnCfg<D>::THREADS);
-  switch (mode) {
-    case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced>), grid, block, 0, stream, a, t); break;
-    case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled>), grid, block, 0, stream, a, t); break;
-    case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore>), grid, block, 0, stream, a, t); break;
-    default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun>), grid, block, 0, stream, a, t); break;
+  const NoSrc none;
+  if (lay.src) {  // shards: product mode only
+    if (mode != kRun) return XSTAGE_ERR_INVALID;
+    hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, true>), grid, block, 0, stream, a, t, *lay.src);
+  } else {
+    switch (mode) {
+      case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced, false>), grid, block, 0, stream, a, t, none); break;
+      case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled, false>), grid, block, 0, stream, a, t, none); break;
+      case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore, false>), grid, block, 0, stream, a, t, none); break;
+      default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, false>), grid, block, 0, stream, a, t, none); break;
+    }
   }
   return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
 }
@@ -663,7 +728,9 @@ int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, in
 }
 
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
-                    int P, float scale, hipStream_t stream, int mode, unsigned long long* stamps) {
+                    int P, float scale, hipStream_t stream, int mode, unsigned long long* stamps, const Layout* layout) {
+  static const Layout kPlain;
+  const Layout& lay = layout ? *layout : kPlain;
   const int n_tiles = B * H * ((S + 127) / 128);
   const int nkv = (S + 63) / 64;
   SplitPlan plan = choose_split(n_tiles, nkv, D, partial_bytes_per_unit(D));
@@ -672,8 +739,8 @@ int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable
                                      &plan.partial, &plan.counters);
     if (st != XSTAGE_OK) return st;
   }
-  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, stream);
-  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, stream);
+  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, stream);
+  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, stream);
 }
 
 }  // namespace xstage

@@ -26,6 +26,23 @@ struct SlabTable {
   uint16_t* p[XSTAGE_MAX_P];
 };
 
+// Sequence shards of q, k and v, read in place (the pre-attention all-to-all): shard p holds
+// rows [p * S/P, (p + 1) * S/P) of every head.  Passed by value in kernel arguments.
+constexpr int kMaxSrc = 32;
+struct SrcTable {
+  const uint16_t* q[kMaxSrc];
+  const uint16_t* k[kMaxSrc];
+  const uint16_t* v[kMaxSrc];
+};
+
+// Where a launch reads its inputs and writes its outputs, beyond the plain layouts
+// (q, k, v contiguous [B, S, H, D]; slabs [B, S/P, H, D]).
+struct Layout {
+  const SrcTable* src = nullptr;  // non-null: inputs are P shards [B, S/P, src_heads, D]
+  int src_heads = 0, src_head0 = 0;  // shard row width (heads) and this call's first head
+  int dst_heads = 0, dst_head0 = 0;  // slab row width (heads) and this call's first column
+};
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 32-lane halves of a wave64 swap: returns, in every lane, max(x[lane], x[lane ^ 32]).

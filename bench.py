@@ -7,8 +7,9 @@ sequence with the post-attention all-to-all written from the epilogue.  Inputs a
 synthetic bf16 tensors resident in HBM before the timed region.  Prints one JSON line.
 
 Extra legs (reported inside the same line): the serial path (attention into a contiguous
-buffer, then the separate scatter kernel), attention alone (P=1), and the CPU oracle timed
-on a bounded sample of the same workload (``cpu_baseline``).  ``--bg`` instead runs the
+buffer, then the separate scatter kernel), attention alone (P=1), the full-head Ulysses
+layouts (strided destination; the whole layer reading its inputs from P sequence shards),
+and the CPU oracle timed on a bounded sample of the same workload (``cpu_baseline``).  ``--bg`` instead runs the
 Burst-Gap store sweep and prints one JSON line per point plus the fitted parameters.
 """
 
@@ -162,6 +163,21 @@ def bench_attention(args, torch, xs):
     ms_attn = timed(attn_only, args.steps, leg_warmup, torch)
     ms_scatter = timed(scatter_only, args.steps, leg_warmup, torch)
 
+    # Full-head Ulysses layouts, as rank 5 of a group of P ranks over H_local * P heads:
+    # the strided epilogue (receive buffers [B, S/P, H, D], this rank's head columns) and the
+    # whole layer with the pre-attention all-to-all read from P sequence shards of all heads
+    # (seeded N(0,1) shards; separate allocations).
+    H_all, h0 = w.H * w.P, min(5, w.P - 1) * w.H
+    recv = [torch.empty((w.B, w.S // w.P, H_all, w.D), dtype=torch.bfloat16, device="cuda") for _ in range(w.P)]
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
+    shards = [[torch.randn((w.B, w.S // w.P, H_all, w.D), generator=gen, device="cuda").to(torch.bfloat16)
+               for _ in range(w.P)] for _ in range(3)]
+    strided = xs.bind("xstage_attn_a2a_fwd_strided", q, k, v, recv, h0, w.scale)
+    layer = xs.bind("xstage_ulysses_attn_fwd", shards[0], shards[1], shards[2], recv, w.H, h0, w.scale)
+    ms_strided = timed(strided, args.steps, leg_warmup, torch)
+    ms_layer = timed(layer, args.steps, leg_warmup, torch)
+    del shards, recv
+
     tflops = w.flops / (ms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
@@ -189,6 +205,12 @@ def bench_attention(args, torch, xs):
         "ms_attention_only": ms_attn,
         "ms_scatter_only": ms_scatter,
         "scatter_GBps": round(2 * w.out_bytes / (ms_scatter * 1e-3) / 1e9, 1),
+        "ulysses_group": f"rank {h0 // w.H} of {w.P}, {H_all} heads, heads [{h0}, {h0 + w.H})",
+        "ms_strided_destination": ms_strided,
+        "strided_vs_fused": round(ms_strided / ms, 4),
+        "ms_ulysses_layer": ms_layer,
+        "ulysses_layer_vs_fused": round(ms_layer / ms, 4),
+        "ulysses_layer_TFLOPs": round(w.flops / (ms_layer * 1e-3) / 1e12, 3),
         "wall_s_timed_region": t_wall,
     }
     hbm = traffic_entry()

@@ -78,6 +78,40 @@ int xstage_attn_a2a_fwd(const void* q, const void* k, const void* v, void* const
 int xstage_attn_fwd(const void* q, const void* k, const void* v, void* out,
                     int B, int S, int H_local, int D, float scale, void* stream);
 
+/* xstage_attn_a2a_fwd with full-head destination buffers ("Contributions",
+ * FlashAttention-A2A item: each output tile is stored straight into its destination's
+ * receive buffer).  In a Ulysses group over H_dst heads, destination p's receive buffer
+ * holds its S/P sequence rows of every head: out_dst[p] is [B, S/P, H_dst, D], and this
+ * call writes head columns [h_dst0, h_dst0 + H_local) only:
+ *   out_dst[p][b][r][h_dst0 + h][d] = O[b][p*S/P + r][h][d];
+ * every other element of out_dst is left untouched.  Requires H_dst >= H_local and
+ * 0 <= h_dst0 <= H_dst - H_local (else XSTAGE_ERR_INVALID), B*S*H_dst*D < 2^31 (else
+ * XSTAGE_ERR_UNSUPPORTED).  The P buffers (B*S*H_dst*D*2/P bytes each) must not overlap
+ * each other or q, k, v.  With H_dst = H_local and h_dst0 = 0 this is xstage_attn_a2a_fwd. */
+int xstage_attn_a2a_fwd_strided(const void* q, const void* k, const void* v, void* const* out_dst,
+                                int B, int S, int H_local, int D, int P, int H_dst, int h_dst0,
+                                float scale, void* stream);
+
+/* One rank's Ulysses attention layer with both all-to-alls fused into the attention kernel
+ * (the post-attention one in the epilogue as in xstage_attn_a2a_fwd_strided, the
+ * pre-attention one in the Q/K/V loads).  Before attention each of the P ranks holds one
+ * contiguous sequence shard of every head; this rank computes the heads
+ * [h0, h0 + H_local) over the whole sequence:
+ *   q_src[p], k_src[p], v_src[p]: HOST arrays of P device pointers, shard p = [B, S/P, H, D]
+ *       holding sequence rows [p*S/P, (p+1)*S/P) of all H heads (read only; shards may
+ *       alias each other);
+ *   out_dst[p]: HOST array of P device pointers, [B, S/P, H, D]; head columns
+ *       [h0, h0 + H_local) are written, all other elements are left untouched:
+ *       out_dst[p][b][r][h0 + h][d] = O[b][p*S/P + r][h][d], with
+ *       O = attention of Q[b][s][h] = q_src[s / (S/P)][b][s % (S/P)][h0 + h] (same for K, V).
+ * Requires 0 < H_local <= H, 0 <= h0 <= H - H_local (else XSTAGE_ERR_INVALID), P <= 32
+ * and B*S*H*D < 2^31 (else XSTAGE_ERR_UNSUPPORTED).  The output buffers must not overlap
+ * each other or any shard.  Same values as gathering the heads into contiguous q, k, v and
+ * calling xstage_attn_a2a_fwd_strided with H_dst = H, h_dst0 = h0, bit for bit. */
+int xstage_ulysses_attn_fwd(const void* const* q_src, const void* const* k_src,
+                            const void* const* v_src, void* const* out_dst, int B, int S, int H,
+                            int H_local, int h0, int D, int P, float scale, void* stream);
+
 /* The separate all-to-all send step of the serial baseline: copies a contiguous
  * [B, S, H_local, D] tensor into the P slabs.  Slabs must not overlap `in` or each other. */
 int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int H_local,

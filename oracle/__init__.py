@@ -14,6 +14,9 @@ Inference", technical summary):
   piggybacking item: fusion only changes who issues the stores and when).  So the oracle is
   the textbook definition, softmax(scale * Q K^T) V, in float64 on the bf16 inputs, then an
   explicit Ulysses slab permutation.
+* ``ulysses``: the pre-attention (sequence -> heads) and post-attention (heads -> sequence)
+  all-to-alls of one rank of a Ulysses group, with full-head shards and receive buffers,
+  as plain loops, and one rank's attention layer built from them.
 * ``burst_gap``: the Burst-Gap issue-time model of the "Methodology" section,
   T_iss(G; K, V) = max(T0_iss(K, V), V / R - G), its two regimes, a labelled fluid-queue
   reading that gives the capacity Q a role, and the parameter fit used on microbenchmark
@@ -34,6 +37,7 @@ from .attention import (  # noqa: F401
     ulysses_gather,
     ulysses_scatter,
 )
+from .ulysses import pre_gather, scatter_heads, ulysses_attention  # noqa: F401
 from .burst_gap import (  # noqa: F401
     fit_burst_gap,
     regime,

@@ -47,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -232,6 +232,59 @@ def test_traced_rejects(L):
     assert f(*args, 0, SLAB0 + 64, None) == INVALID            # stamps inside a slab
     assert f(Q, K, V, arr, 1, 256, 2, 64, 2, float("nan"), 0, STAMPS, None) == INVALID
     assert f(Q, K, V, arr, 1, 255, 2, 64, 2, 0.125, 0, STAMPS, None) == INVALID
+
+
+@no_device
+def test_strided_rejects(L):
+    f = L.xstage_attn_a2a_fwd_strided
+    arr, keep = _lib.ptr_array(slabs(2))
+
+    def call(H=2, P=2, H_dst=8, h0=4, q=Q, sl=arr, S=256, scale=0.125):
+        return f(q, K, V, sl, 1, S, H, 64, P, H_dst, h0, scale, None)
+
+    assert call(H_dst=1) == INVALID            # fewer destination heads than local heads
+    assert call(h0=-1) == INVALID
+    assert call(h0=7) == INVALID               # columns 7, 8 past H_dst = 8
+    assert call(sl=None) == INVALID
+    assert call(q=0) == INVALID
+    assert call(S=255) == INVALID              # S % P
+    assert call(scale=float("nan")) == INVALID
+    assert call(H_dst=1 << 17, h0=0) == UNSUPPORTED  # destination offsets reach 2^31 elements
+    near, keep2 = _lib.ptr_array([SLAB0, SLAB0 + 256 * 8 * 64 - 16])  # slab 0 spans 256*8*64*2/2 bytes
+    assert call(sl=near) == INVALID
+    inq, keep3 = _lib.ptr_array([SLAB0, Q + 64])
+    assert call(sl=inq) == INVALID
+
+
+@no_device
+def test_ulysses_rejects(L):
+    f = L.xstage_ulysses_attn_fwd
+    P = 4
+    qs = [0x10_0000_0000 + p * GAP for p in range(P)]
+    ks = [0x20_0000_0000 + p * GAP for p in range(P)]
+    vs = [0x30_0000_0000 + p * GAP for p in range(P)]
+    ds = slabs(P)
+
+    def call(q=qs, k=ks, v=vs, d=ds, B=1, S=256, H=8, Hl=2, h0=2, D=64, P=P, scale=0.125):
+        arrs = [_lib.ptr_array(x) if x is not None else (None, None) for x in (q, k, v, d)]
+        return f(arrs[0][0], arrs[1][0], arrs[2][0], arrs[3][0], B, S, H, Hl, h0, D, P, scale, None)
+
+    assert call(Hl=0) == INVALID
+    assert call(Hl=9) == INVALID
+    assert call(h0=7) == INVALID
+    assert call(h0=-1) == INVALID
+    assert call(S=258) == INVALID
+    assert call(D=96) == UNSUPPORTED
+    assert call(q=None) == INVALID
+    assert call(d=None) == INVALID
+    assert call(q=[qs[0], 0, qs[2], qs[3]]) == INVALID
+    assert call(v=[vs[0], vs[1] + 8, vs[2], vs[3]]) == INVALID
+    assert call(d=[ds[0], ds[1], ds[2], ks[1] + 16]) == INVALID     # output overlaps a K shard
+    assert call(d=[ds[0], ds[0] + 64, ds[2], ds[3]]) == INVALID     # outputs overlap
+    assert call(scale=float("inf")) == INVALID
+    big = [SLAB0 + p * GAP for p in range(33)]
+    assert call(q=big, k=big, v=big, d=big, S=33 * 8, P=33) == UNSUPPORTED  # more than 32 shards
+    assert call(H=1 << 14, Hl=2, h0=0, S=1 << 14, D=128, P=4) == UNSUPPORTED
 
 
 @no_device
