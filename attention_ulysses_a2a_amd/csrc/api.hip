@@ -157,7 +157,7 @@ int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, int cap, int* til
 int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
                                int H_local, int D, int P, float scale, int mode, unsigned long long* stamps,
                                void* stream) {
-  if (mode < 0 || mode > 2 || stamps == nullptr || (reinterpret_cast<uintptr_t>(stamps) & 7u) != 0)
+  if (mode < 0 || mode > 3 || stamps == nullptr || (reinterpret_cast<uintptr_t>(stamps) & 7u) != 0)
     return XSTAGE_ERR_INVALID;
   int st = check_shape(B, S, H_local, D, P);
   if (st != XSTAGE_OK) return st;

@@ -77,6 +77,7 @@ struct AttnArgs {
   f32x4* partial;    // split partials: [tile][split][wave][chunk][64 lanes] (n_split > 1)
   uint32_t* counters;  // per-tile arrival counters, zero between launches (n_split > 1)
   unsigned long long* stamps;  // traced modes: [workgroup][wave][4] wall-clock ticks
+  int clock_stamps;  // traced modes: entries 2, 3 hold shader-clock ticks at start / loop end
 };
 
 // Kernel modes.  kRun is the product path.  The traced modes record, per wave, the
@@ -86,6 +87,8 @@ struct AttnArgs {
 // counterfactual: the issuer blocks until its stores are visible); kNoStore issues no output
 // store at all (the unbounded-asynchronous bound: stores cost nothing; nothing is written).
 enum AttnMode { kRun = 0, kTraced = 1, kCoupled = 2, kNoStore = 3 };
+// Host-side launch mode: kTraced with shader-clock stamps in entries 2 and 3.
+constexpr int kTracedClock = 4;
 
 // A pointer read through a wave-uniform index, kept in scalar registers.
 __device__ __forceinline__ uint16_t* uniform_ptr(uint16_t* p) {
@@ -127,16 +130,19 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int hl = lane >> 5;  // half of the wave
-  unsigned long long t_start = 0, t_loop = 0;
-  if constexpr (MODE != kRun) t_start = __builtin_amdgcn_s_memrealtime();
+  unsigned long long t_start = 0, t_loop = 0, c_start = 0, c_loop = 0;
+  if constexpr (MODE != kRun) {
+    t_start = __builtin_amdgcn_s_memrealtime();
+    c_start = __builtin_amdgcn_s_memtime();
+  }
   auto trace_out = [&](unsigned long long t_issued, unsigned long long t_done) {
     if constexpr (MODE != kRun) {
       if (lane == 0) {
         unsigned long long* st = a.stamps + ((size_t)blockIdx.x * 4 + w) * 4;
         st[0] = t_start;
         st[1] = t_loop;
-        st[2] = t_issued;
-        st[3] = t_done;
+        st[2] = a.clock_stamps ? c_start : t_issued;
+        st[3] = a.clock_stamps ? c_loop : t_done;
       }
     }
   };
@@ -216,9 +222,18 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   // built per block from the shard pointer (kernel arguments, scalar loads); the tables
   // index 0 = K, 1 = V.
   __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+  // Shard cursors (SRC): first row of the shard holding the K (V) stream's current block and
+  // that shard's resource; blocks only move forward, from j0.
+  int k_lo = 0, v_lo = 0;
+  __amdgpu_buffer_rsrc_t k_r, v_r;
   if constexpr (!SRC) {
     krsrc = make_rsrc(a.k);
     vrsrc = make_rsrc(a.v);
+  } else {
+    const int p = j0 * C::BN / a.src_rows;
+    k_lo = v_lo = p * a.src_rows;
+    k_r = make_rsrc(uniform_ptr(src.k[p]));
+    v_r = make_rsrc(uniform_ptr(src.v[p]));
   }
   uint32_t ld_voff[C::NLD];  // byte offset of this lane's chunk from the block's first key
 #pragma unroll
@@ -236,26 +251,42 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
             rsrc, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
             ld_voff[i] + boff, 0, 0, 0);
     } else {
-      // Rows n0 .. n0+63 come from shards p0 .. p1 (one, unless the block straddles a shard
-      // boundary).  The last shard also takes the rows past S, which lie beyond its range
-      // and read as zeros.  A lane loads from exactly one shard, so every LDS chunk is
-      // written once.
-      const uint16_t* const* tbl = slot_byte < 2 * C::BLKB ? src.k : src.v;
+      // The stream's cursor (K or V: which one is fixed by the slot, a constant after
+      // inlining) names the shard holding its current block.  A block inside that shard is
+      // one resource; the rows past S of the last block lie beyond the last shard's range
+      // and read as zeros.  A block reaching into the next shard(s) loads from shards
+      // p0 .. p1, each lane from exactly one of them (every LDS chunk written once), and
+      // moves the cursor to the shard of its last row.
+      const bool is_k = slot_byte < 2 * C::BLKB;
+      int& cur_lo = is_k ? k_lo : v_lo;
+      __amdgpu_buffer_rsrc_t& cur_r = is_k ? k_r : v_r;
       const int last = min(n0 + C::BN, S) - 1;
-      const int p0 = n0 / a.src_rows, p1 = last / a.src_rows;
-      for (int p = p0; p <= p1; ++p) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(tbl[p]));
-        const int lo = p * a.src_rows - n0;                        // first block row in shard p
-        const int hi = p == p1 ? C::BN : (p + 1) * a.src_rows - n0;  // one past its last
-        const uint32_t boff = (uint32_t)(n0 - p * a.src_rows) * rs * 2u;
+      if (last < cur_lo + a.src_rows) {
+        const uint32_t boff = (uint32_t)(n0 - cur_lo) * rs * 2u;
 #pragma unroll
-        for (int i = 0; i < C::NLD; ++i) {
-          const int row = ((i * 4 + w) * 64 + lane) / C::CH;
-          if (p0 == p1 || (row >= lo && row < hi))
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
-                ld_voff[i] + boff, 0, 0, 0);
+        for (int i = 0; i < C::NLD; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              cur_r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
+              ld_voff[i] + boff, 0, 0, 0);
+      } else {
+        const uint16_t* const* tbl = is_k ? src.k : src.v;
+        const int p0 = n0 / a.src_rows, p1 = last / a.src_rows;
+        for (int p = p0; p <= p1; ++p) {
+          const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(tbl[p]));
+          const int lo = p * a.src_rows - n0;                        // first block row in shard p
+          const int hi = p == p1 ? C::BN : (p + 1) * a.src_rows - n0;  // one past its last
+          const uint32_t boff = (uint32_t)(n0 - p * a.src_rows) * rs * 2u;
+#pragma unroll
+          for (int i = 0; i < C::NLD; ++i) {
+            const int row = ((i * 4 + w) * 64 + lane) / C::CH;
+            if (row >= lo && row < hi)
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                  r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
+                  ld_voff[i] + boff, 0, 0, 0);
+          }
         }
+        cur_lo = p1 * a.src_rows;
+        cur_r = make_rsrc(uniform_ptr(tbl[p1]));
       }
     }
   };
@@ -455,7 +486,10 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
     last_block(j, s_a, VSLOT0);
   }
 
-  if constexpr (MODE != kRun) t_loop = __builtin_amdgcn_s_memrealtime();
+  if constexpr (MODE != kRun) {
+    t_loop = __builtin_amdgcn_s_memrealtime();
+    c_loop = __builtin_amdgcn_s_memtime();
+  }
 
   // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
   // merges them (rescaling by exp2(m_s - m)) and runs the epilogue for the tile.
@@ -665,6 +699,8 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.partial = static_cast<f32x4*>(plan.partial);
   a.counters = plan.counters;
   a.stamps = stamps;
+  a.clock_stamps = mode == kTracedClock;
+  if (mode == kTracedClock) mode = kTraced;
   a.src_rows = lay.src ? S / P : S;
   a.src_hs = lay.src_heads > 0 ? lay.src_heads : H;
   a.src_h0 = lay.src_head0;

@@ -13,7 +13,8 @@ back-to-back launches, inputs resident):
   * t_fused     the fused kernel (xstage_attn_a2a_fwd);
   * t_nostore   the unbounded-asynchronous bound: the traced kernel issuing no output store;
   * t_coupled   the completion-coupled counterfactual: every wave waits for its stores;
-and, from the traced kernel's per-wave stamps, the epilogue span (end of the key loop to the
+the core clock of the key loops (traced mode 3) and, from the traced kernel's per-wave
+stamps, the epilogue span (end of the key loop to the
 last store issued; includes the merge of key splits) and, in the coupled mode, the drain
 span (last store issued to stores complete).  The completion-coupled model predicts
 t_fused + rounds * drain, with rounds = workgroups per co-resident slot.
@@ -44,6 +45,17 @@ def spans_from_stamps(stamps: np.ndarray, hz: float):
     done = emit & (st[:, 3] > 0)
     drain = (st[done, 3] - st[done, 2]) / hz
     return epi, drain
+
+
+def loop_clock_ghz(stamps: np.ndarray, hz: float, min_wall_s: float = 2e-6):
+    """Median core clock over the waves' key loops from mode-3 stamps ([1]-[0] wall-clock
+    ticks, [3]-[2] shader-clock ticks), over loops of at least ``min_wall_s``."""
+    st = stamps.reshape(-1, 4).astype(np.int64)
+    wall = (st[:, 1] - st[:, 0]) / hz
+    use = wall >= min_wall_s
+    if not use.any():
+        return None
+    return float(np.median((st[use, 3] - st[use, 2]) / wall[use]) / 1e9)
 
 
 def _time(torch, fn, n, warm):
@@ -79,19 +91,21 @@ def run_study(torch, xs, S_list=DEFAULT_S, H=3, D=128, P=8, seed=11, target_s=0.
         sl = [slabs[p] for p in range(P)]
         out1 = torch.empty((1, S, H, D), dtype=torch.bfloat16, device="cuda")
         nwg, nsp = xs.xstage_attn_a2a_plan(1, S, H, D)
-        stamps = [torch.zeros(nwg * 16, dtype=torch.int64, device="cuda") for _ in range(3)]
+        stamps = [torch.zeros(nwg * 16, dtype=torch.int64, device="cuda") for _ in range(4)]
         calls = {
             "attn": xs.bind("xstage_attn_fwd", q, k, v, out1, w.scale),
             "fused": xs.bind("xstage_attn_a2a_fwd", q, k, v, sl, w.scale),
             "traced": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 0, stamps[0], w.scale),
             "coupled": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 1, stamps[1], w.scale),
             "nostore": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 2, stamps[2], w.scale),
+            "clock": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 3, stamps[3], w.scale),
         }
         t_est = _time(torch, calls["fused"], 3, 3)
         n = max(20, min(2000, int(target_s / max(t_est, 1e-6))))
         t = {name: _time(torch, fn, n, max(50, n // 4)) for name, fn in calls.items()}
         epi, _ = spans_from_stamps(stamps[0].cpu().numpy(), hz)
         _, drain = spans_from_stamps(stamps[1].cpu().numpy(), hz)
+        ghz = loop_clock_ghz(stamps[3].cpu().numpy(), hz)
         rounds = nwg / slots
         drain_med = float(np.median(drain)) if len(drain) else 0.0
         row = {
@@ -106,6 +120,7 @@ def run_study(torch, xs, S_list=DEFAULT_S, H=3, D=128, P=8, seed=11, target_s=0.
             "drain_span_us_median": drain_med * 1e6,
             "drain_span_us_p90": float(np.percentile(drain, 90)) * 1e6 if len(drain) else None,
             "coupled_model_us": coupled_prediction(t["fused"], math.ceil(rounds), drain_med) * 1e6,
+            "loop_clock_ghz": ghz,
             "iterations": n,
         }
         rows.append(row)

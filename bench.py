@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused attn+A2A-scatter TFLOP/s & % bf16 MFMA peak (S=4608, 1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+PEAK_CLOCK_GHZ = 2.4           # engine clock the published peak assumes (256 CUs x 4096 FLOP/clk)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_a2a_flux1024.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_ulysses_a2a_amd", "csrc", f)
                   for f in ("attn_a2a.hip", "common.hpp")]
@@ -178,6 +179,22 @@ def bench_attention(args, torch, xs):
     ms_layer = timed(layer, args.steps, leg_warmup, torch)
     del shards, recv
 
+    # Core clock during the key loop (traced call, mode 3: shader-clock ticks against
+    # wall-clock ticks per wave), right after back-to-back fused launches: the published
+    # peak assumes 2.4 GHz, while a chip running dense MFMA work clocks lower.
+    nwg, _ = xs.xstage_attn_a2a_plan(w.B, w.S, w.H, w.D)
+    stamps = torch.zeros(nwg * 16, dtype=torch.int64, device="cuda")
+    clocked = xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, slab_list, 3, stamps, w.scale)
+    for _ in range(args.warmup):
+        fused()
+    clocked()
+    torch.cuda.synchronize()
+    st = stamps.cpu().numpy().reshape(nwg, 4, 4).astype(np.int64)
+    wall = (st[:, :, 1] - st[:, :, 0]) / xs.xstage_wallclock_hz()
+    ticks = st[:, :, 3] - st[:, :, 2]
+    use = wall > 2e-6
+    loop_ghz = float(np.median(ticks[use] / wall[use]) / 1e9) if use.any() else None
+
     tflops = w.flops / (ms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
@@ -212,6 +229,9 @@ def bench_attention(args, torch, xs):
         "ulysses_layer_vs_fused": round(ms_layer / ms, 4),
         "ulysses_layer_TFLOPs": round(w.flops / (ms_layer * 1e-3) / 1e12, 3),
         "wall_s_timed_region": t_wall,
+        "loop_clock_ghz": None if loop_ghz is None else round(loop_ghz, 3),
+        "pct_of_peak_at_loop_clock": None if loop_ghz is None else
+        round(100.0 * tflops / (PEAK_BF16_TFLOPS * loop_ghz / PEAK_CLOCK_GHZ), 2),
     }
     hbm = traffic_entry()
     res["roofline"] = {

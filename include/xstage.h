@@ -152,11 +152,14 @@ int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, int cap, int* til
  *           complete before it ends;
  *   mode 2: unbounded-asynchronous bound: no output store is issued at all (the slabs are
  *           NOT written; everything else runs);
+ *   mode 3: as mode 0, but stamp entries [2] and [3] hold the shader-clock counter
+ *           (s_memtime) at start and at the end of the key loop, so that
+ *           ([3] - [2]) / ([1] - [0]) * xstage_wallclock_hz is the core clock the loop ran at;
  *   stamps: device uint64 [n_workgroups][4 waves][4] (xstage_attn_a2a_plan), caller-owned,
  *           8-byte aligned, disjoint from every other argument; per wave, in wall-clock
  *           ticks (xstage_wallclock_hz): start, end of the key loop, last epilogue store
  *           issued (0 if the wave stores nothing: a split that does not merge, rows past S,
- *           mode 2), stores complete (mode 1 only, else 0).
+ *           mode 2), stores complete (mode 1 only, else 0); mode 3 as stated above.
  * Other modes are XSTAGE_ERR_INVALID. */
 int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void* const* out_slabs,
                                int B, int S, int H_local, int D, int P, float scale, int mode,

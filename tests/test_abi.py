@@ -224,7 +224,7 @@ def test_traced_rejects(L):
     arr, keep = _lib.ptr_array(slabs(2))
     f = L.xstage_attn_a2a_fwd_traced
     args = (Q, K, V, arr, 1, 256, 2, 64, 2, 0.125)
-    assert f(*args, 3, STAMPS, None) == INVALID                # unknown mode
+    assert f(*args, 4, STAMPS, None) == INVALID                # unknown mode
     assert f(*args, -1, STAMPS, None) == INVALID
     assert f(*args, 0, 0, None) == INVALID                     # no stamps
     assert f(*args, 0, STAMPS + 4, None) == INVALID            # misaligned stamps

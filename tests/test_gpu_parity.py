@@ -263,9 +263,10 @@ def test_bound_launches_equal_direct_calls():
 
 @pytest.mark.parametrize("name", ["tiny", "flux1024"])
 def test_traced_modes(name):
-    """The instrumented call: modes 0 and 1 write the fused result bit for bit, mode 2 writes
-    nothing; per-wave stamps are ordered, and exactly the waves owning output rows of a
-    merged (or unsplit) tile record a store."""
+    """The instrumented call: modes 0, 1 and 3 write the fused result bit for bit, mode 2
+    writes nothing; per-wave stamps are ordered, exactly the waves owning output rows of a
+    merged (or unsplit) tile record a store, and mode 3's shader-clock ticks give a
+    plausible core clock."""
     w = workload(name)
     qb, kb, vb = make_inputs(w)
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
@@ -292,3 +293,15 @@ def test_traced_modes(name):
             assert np.all(st[emit][:, 3] >= st[emit][:, 2]) and np.all(st[emit][:, 3] > 0)
         else:
             assert np.all(st[:, :, 3] == 0)
+    # mode 3: the fused result, and shader-clock ticks at start / loop end in entries 2, 3
+    g = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
+    stamps = torch.zeros(nwg * 16, dtype=torch.int64, device="cuda")
+    xs.xstage_attn_a2a_fwd_traced(q, k, v, g.views, 3, stamps, w.scale)
+    torch.cuda.synchronize()
+    assert g.guards_intact() and np.array_equal(g.slabs_host(), ref)
+    st = stamps.cpu().numpy().reshape(nwg, 4, 4).astype(np.int64)
+    assert np.all(st[:, :, 3] >= st[:, :, 2]) and np.all(st[:, :, 2] > 0)
+    long = (st[:, :, 1] - st[:, :, 0]) > 200  # loops of >= 2 us of wall clock
+    ghz = (st[:, :, 3] - st[:, :, 2])[long] / ((st[:, :, 1] - st[:, :, 0])[long] / xs.xstage_wallclock_hz()) / 1e9
+    log(f"[{name}] shader clock during the key loop: median {np.median(ghz) if ghz.size else float('nan'):.3f} GHz")
+    assert ghz.size == 0 or (0.3 < np.median(ghz) < 3.5)

@@ -1,8 +1,10 @@
 """Host-side pieces of the store-span study (no GPU): the completion-coupled prediction and
-the span extraction from per-wave stamps."""
+the span extraction and the loop clock from per-wave stamps."""
 
 import numpy as np
+import pytest
 
+from attention_ulysses_a2a_amd import xstage_study
 from attention_ulysses_a2a_amd.xstage_study import coupled_prediction, spans_from_stamps
 
 
@@ -21,3 +23,12 @@ def test_spans_from_stamps():
     epi, drain = spans_from_stamps(st, hz)
     assert np.allclose(sorted(epi), [1.5e-6, 2.0e-6])
     assert np.allclose(drain, [2.0e-6])
+
+
+def test_loop_clock_from_stamps():
+    hz = 100e6
+    # two waves: 10 us of wall clock with 20000 and 18000 shader ticks (2.0 and 1.8 GHz); a
+    # third with a 1 us loop is below the minimum span and ignored
+    st = np.array([[0, 1000, 5, 20005], [10, 1010, 0, 18000], [0, 100, 0, 99999]], dtype=np.int64)
+    assert xstage_study.loop_clock_ghz(st, hz) == pytest.approx(1.9)
+    assert xstage_study.loop_clock_ghz(st[2:], hz) is None
