@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     XSTAGE_MAX_P,
     XSTAGE_OK,
     BGParams,
+    MoeParams,
     LibraryMissing,
     XStageError,
     lib,
@@ -39,6 +40,8 @@ __all__ = [
     "xstage_attn_a2a_plan",
     "xstage_attn_a2a_schedule",
     "xstage_attn_a2a_fwd_traced",
+    "xstage_moe_waves_run",
+    "xstage_moe_waves_plan",
     "xstage_burst_gap_run",
     "xstage_wallclock_hz",
     "xstage_bg_t_iss",
@@ -263,6 +266,61 @@ def xstage_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, str
     _check(st, "xstage_attn_a2a_fwd_traced")
 
 
+def _int_array(vals):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int * max(1, len(vals)))(*vals)
+
+
+def xstage_moe_waves_plan(expert_offsets, d_model, d_ff, experts_per_wave, schedule):
+    """(l1_launch, l2_launch, n_launches, n_tiles) of a schedule; see include/xstage.h."""
+    offs = _int_array(expert_offsets)
+    E = len(expert_offsets) - 1
+    l1, l2 = (ctypes.c_int * max(1, E))(), (ctypes.c_int * max(1, E))()
+    nl, nt = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().xstage_moe_waves_plan(E, offs, int(d_model), int(d_ff), int(experts_per_wave), int(schedule), l1, l2,
+                                       ctypes.byref(nl), ctypes.byref(nt)), "xstage_moe_waves_plan")
+    return list(l1)[:E], list(l2)[:E], nl.value, nt.value
+
+
+def _moe_call(x, w1, w2, h, expert_offsets, dst_slab, dst_row, outs, experts_per_wave, schedule, stamps, stream):
+    import torch
+
+    for t, name in ((x, "x"), (w1, "w1"), (w2, "w2"), (h, "h")):
+        _dev_tensor(t, name)
+    for t, name in ((dst_slab, "dst_slab"), (dst_row, "dst_row")):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if x.dim() != 2 or w1.dim() != 3 or w2.dim() != 3 or h.dim() != 2:
+        raise ValueError("x [T, d_model], w1 [E, d_ff, d_model], w2 [E, d_model, d_ff], h [T, d_ff]")
+    E, d_ff, d_model = (int(d) for d in w1.shape)
+    outs = list(outs)
+    for i, o in enumerate(outs):
+        _dev_tensor(o, f"outs[{i}]")
+    offs = _int_array(expert_offsets)
+    if len(expert_offsets) != E + 1:
+        raise ValueError("expert_offsets must have E + 1 entries")
+    out_arr, keep = ptr_array([o.data_ptr() for o in outs])
+    rows = _int_array([o.shape[0] if o.dim() == 2 else 0 for o in outs])
+    prm = MoeParams(E, d_model, d_ff, int(experts_per_wave), int(schedule), offs, x.data_ptr(), w1.data_ptr(),
+                    w2.data_ptr(), h.data_ptr(), dst_slab.data_ptr(), dst_row.data_ptr(), len(outs), out_arr, rows,
+                    stamps.data_ptr() if stamps is not None else None)
+    return prm, (offs, keep, rows, x, w1, w2, h, dst_slab, dst_row, outs, stamps), _stream_of(x, stream)
+
+
+def xstage_moe_waves_run(x, w1, w2, h, expert_offsets, dst_slab, dst_row, outs, experts_per_wave, schedule,
+                         stamps=None, stream=None) -> None:
+    """Expert-wave grouped GEMM with the combine all-to-all in the Linear-2 epilogue; see
+    include/xstage.h (outs: P device tensors [rows_p, d_model])."""
+    import torch
+
+    prm, keep, st_ = _moe_call(x, w1, w2, h, expert_offsets, dst_slab, dst_row, outs, experts_per_wave, schedule,
+                               stamps, stream)
+    with torch.cuda.device(x.device):
+        st = lib().xstage_moe_waves_run(ctypes.byref(prm), st_)
+    del keep
+    _check(st, "xstage_moe_waves_run")
+
+
 def xstage_burst_gap_run(K, V_bytes, gap_fma_iters, rounds, dst, stamps, n_dst_sets=1, nontemporal=False,
                          stream=None) -> None:
     """Burst-Gap store microbenchmark; ``stamps`` is an int64 device tensor of K*rounds*3 entries."""
@@ -317,8 +375,8 @@ def bind(name: str, *args, **kwargs) -> _Bound:
     current stream of the tensors' device unless ``stream`` is given), and the calls must be
     made with that device current.  Supported: xstage_attn_a2a_fwd, xstage_attn_fwd,
     xstage_a2a_scatter, xstage_attn_a2a_unfused, xstage_attn_a2a_fwd_traced,
-    xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd, with the same arguments as the
-    functions.
+    xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd, xstage_moe_waves_run, with the same
+    arguments as the functions.
     """
     import torch
 
@@ -377,6 +435,13 @@ def bind(name: str, *args, **kwargs) -> _Bound:
         scale, stream = kwargs.get("scale", args[6] if len(args) > 6 else None), kwargs.get("stream")
         call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
         refs = (q_src, k_src, v_src, out_dst, keep)
+    elif name == "xstage_moe_waves_run":
+        x, w1, w2, h, expert_offsets, dst_slab, dst_row, outs, epw, schedule = args[:10]
+        stamps, stream = kwargs.get("stamps", args[10] if len(args) > 10 else None), kwargs.get("stream")
+        prm, keep, st_ = _moe_call(x, w1, w2, h, expert_offsets, dst_slab, dst_row, outs, epw, schedule, stamps,
+                                   stream)
+        call = (ctypes.byref(prm), st_)
+        refs, dev = (prm, keep), x.device
     else:
         raise ValueError(f"bind: unsupported entry point {name!r}")
     if torch.cuda.current_device() != dev.index:

@@ -28,6 +28,29 @@ class XStageError(RuntimeError):
         super().__init__(f"{where}: {status_name(status)} ({status})")
 
 
+class MoeParams(ctypes.Structure):
+    """Mirror of xstage_moe_params_t."""
+
+    _fields_ = [
+        ("E", ctypes.c_int),
+        ("d_model", ctypes.c_int),
+        ("d_ff", ctypes.c_int),
+        ("experts_per_wave", ctypes.c_int),
+        ("schedule", ctypes.c_int),
+        ("expert_offsets", ctypes.POINTER(ctypes.c_int)),
+        ("x", ctypes.c_void_p),
+        ("w1", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("h", ctypes.c_void_p),
+        ("dst_slab", ctypes.c_void_p),
+        ("dst_row", ctypes.c_void_p),
+        ("P", ctypes.c_int),
+        ("out", ctypes.POINTER(ctypes.c_void_p)),
+        ("out_rows", ctypes.POINTER(ctypes.c_int)),
+        ("stamps", ctypes.c_void_p),
+    ]
+
+
 class BGParams(ctypes.Structure):
     """Mirror of xstage_bg_params_t."""
 
@@ -57,6 +80,8 @@ SIGNATURES = {
     "xstage_attn_a2a_plan": (_i, [_i, _i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "xstage_attn_a2a_schedule": (_i, [_i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 5),
     "xstage_attn_a2a_fwd_traced": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp, _vp]),
+    "xstage_moe_waves_run": (_i, [ctypes.POINTER(MoeParams), _vp]),
+    "xstage_moe_waves_plan": (_i, [_i, ctypes.POINTER(_i), _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 4),
     "xstage_burst_gap_run": (_i, [ctypes.POINTER(BGParams), _vp]),
     "xstage_wallclock_hz": (_i, [ctypes.POINTER(ctypes.c_double)]),
     "xstage_bg_t_iss": (ctypes.c_double, [ctypes.c_double] * 4),

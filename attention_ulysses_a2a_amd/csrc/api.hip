@@ -4,7 +4,10 @@
 
 #include <cmath>
 
+#include <vector>
+
 #include "common.hpp"
+#include "moe_waves.hpp"
 #include "validate.hpp"
 
 namespace xstage {
@@ -170,6 +173,98 @@ int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void
   if (st != XSTAGE_OK) return st;
   return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale,
                          static_cast<hipStream_t>(stream), 1 + mode, stamps);
+}
+
+static int check_moe_shape(int E, const int* offsets, int d_model, int d_ff, int epw, int schedule,
+                           std::vector<int>* rows) {
+  if (E < 1 || offsets == nullptr || epw < 1 || (schedule != 0 && schedule != 1)) return XSTAGE_ERR_INVALID;
+  if (E > 4096 || epw > kMoeMaxWaveExperts) return XSTAGE_ERR_UNSUPPORTED;
+  if (d_model <= 0 || d_ff <= 0 || d_model % 128 != 0 || d_ff % 128 != 0) return XSTAGE_ERR_INVALID;
+  if (d_model > 65536 || d_ff > 65536) return XSTAGE_ERR_UNSUPPORTED;
+  if (offsets[0] != 0) return XSTAGE_ERR_INVALID;
+  rows->resize(E);
+  for (int e = 0; e < E; ++e) {
+    if (offsets[e + 1] < offsets[e]) return XSTAGE_ERR_INVALID;
+    (*rows)[e] = offsets[e + 1] - offsets[e];
+  }
+  return XSTAGE_OK;
+}
+
+static int moe_total_tiles(int E, const std::vector<int>& rows, int d_model, int d_ff) {
+  long long n = 0;
+  for (int e = 0; e < E; ++e) n += moe_tiles(rows[e], d_ff) + moe_tiles(rows[e], d_model);
+  return n > (1 << 30) ? -1 : (int)n;
+}
+
+int xstage_moe_waves_plan(int E, const int* expert_offsets, int d_model, int d_ff, int experts_per_wave, int schedule,
+                          int* l1_launch, int* l2_launch, int* n_launches, int* n_tiles) {
+  std::vector<int> rows;
+  const int st = check_moe_shape(E, expert_offsets, d_model, d_ff, experts_per_wave, schedule, &rows);
+  if (st != XSTAGE_OK) return st;
+  if (!l1_launch || !l2_launch || !n_launches || !n_tiles) return XSTAGE_ERR_INVALID;
+  const int nt = moe_total_tiles(E, rows, d_model, d_ff);
+  if (nt < 0) return XSTAGE_ERR_UNSUPPORTED;
+  MoeShape sh = {E, d_model, d_ff, experts_per_wave, expert_offsets, rows.data()};
+  std::vector<MoeLaunch> plan;
+  *n_launches = moe_plan(sh, schedule, &plan);
+  for (int i = 0; i < (int)plan.size(); ++i) {
+    for (int e = plan[i].l1_begin; e < plan[i].l1_end; ++e) l1_launch[e] = i;
+    for (int e = plan[i].l2_begin; e < plan[i].l2_end; ++e) l2_launch[e] = i;
+  }
+  *n_tiles = nt;
+  return XSTAGE_OK;
+}
+
+int xstage_moe_waves_run(const xstage_moe_params_t* p, void* stream) {
+  if (p == nullptr) return XSTAGE_ERR_INVALID;
+  std::vector<int> rows;
+  int st = check_moe_shape(p->E, p->expert_offsets, p->d_model, p->d_ff, p->experts_per_wave, p->schedule, &rows);
+  if (st != XSTAGE_OK) return st;
+  if (p->P < 1) return XSTAGE_ERR_INVALID;
+  if (p->P > XSTAGE_MAX_P) return XSTAGE_ERR_UNSUPPORTED;
+  const void* bf[4] = {p->x, p->w1, p->w2, p->h};
+  for (const void* q : bf)
+    if (q == nullptr || !aligned16(q)) return XSTAGE_ERR_INVALID;
+  if (!p->dst_slab || !p->dst_row || (reinterpret_cast<uintptr_t>(p->dst_slab) & 3u) ||
+      (reinterpret_cast<uintptr_t>(p->dst_row) & 3u) || !p->out || !p->out_rows)
+    return XSTAGE_ERR_INVALID;
+  if (p->stamps && (reinterpret_cast<uintptr_t>(p->stamps) & 7u)) return XSTAGE_ERR_INVALID;
+  const int nt = moe_total_tiles(p->E, rows, p->d_model, p->d_ff);
+  if (nt < 0) return XSTAGE_ERR_UNSUPPORTED;
+  const unsigned long long T = (unsigned long long)p->expert_offsets[p->E];
+  const unsigned long long E = (unsigned long long)p->E, dm = p->d_model, df = p->d_ff;
+  // Everything read, then everything written: each written range must be disjoint from all.
+  std::vector<Range> reads = {range_of(p->x, T * dm * 2), range_of(p->w1, E * df * dm * 2),
+                              range_of(p->w2, E * dm * df * 2), range_of(p->dst_slab, T * 4),
+                              range_of(p->dst_row, T * 4)};
+  std::vector<Range> writes = {range_of(p->h, T * df * 2)};
+  for (int q = 0; q < p->P; ++q) {
+    if (p->out[q] == nullptr || !aligned16(p->out[q]) || p->out_rows[q] < 0) return XSTAGE_ERR_INVALID;
+    writes.push_back(range_of(p->out[q], (unsigned long long)p->out_rows[q] * dm * 2));
+  }
+  if (p->stamps) writes.push_back(range_of(p->stamps, (unsigned long long)nt * 16 * 8));
+  for (size_t a = 0; a < writes.size(); ++a) {
+    for (const Range& r : reads)
+      if (overlaps(writes[a], r)) return XSTAGE_ERR_INVALID;
+    for (size_t b = 0; b < a; ++b)
+      if (overlaps(writes[a], writes[b])) return XSTAGE_ERR_INVALID;
+  }
+  if (T == 0) return XSTAGE_OK;
+  MoeShape sh = {p->E, p->d_model, p->d_ff, p->experts_per_wave, p->expert_offsets, rows.data()};
+  MoeBuffers buf = {};
+  buf.x = static_cast<const uint16_t*>(p->x);
+  buf.w1 = static_cast<const uint16_t*>(p->w1);
+  buf.w2 = static_cast<const uint16_t*>(p->w2);
+  buf.h = static_cast<uint16_t*>(p->h);
+  buf.dst_slab = p->dst_slab;
+  buf.dst_row = p->dst_row;
+  buf.P = p->P;
+  for (int q = 0; q < p->P; ++q) {
+    buf.out[q] = static_cast<uint16_t*>(p->out[q]);
+    buf.out_rows[q] = p->out_rows[q];
+  }
+  buf.stamps = p->stamps;
+  return launch_moe(sh, buf, p->schedule, static_cast<hipStream_t>(stream));
 }
 
 int xstage_burst_gap_run(const xstage_bg_params_t* p, void* stream) {

@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--bg", action="store_true", help="run the Burst-Gap store sweep instead")
     ap.add_argument("--xstage-study", action="store_true",
                     help="fused-epilogue overhead and store spans against sequence length (one JSON line per S)")
+    ap.add_argument("--moe", action="store_true",
+                    help="expert-wave grouped-GEMM stand-in: expert waves vs interleaved schedule")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the scatter kernel on a 512 MiB input (reference for HBM byte counters)")
     return ap.parse_args()
@@ -245,6 +247,58 @@ def bench_attention(args, torch, xs):
     return w, (qb, kb, vb), res
 
 
+def bench_moe(args, torch, xs):
+    """Both schedules of the expert-wave stand-in on the DeepSeek-V3-sized expert layer
+    (32 experts in waves of 8, d_model 7168, d_ff 2048, ~256 token rows per expert, 8
+    destinations): one step is the whole layer (all launches of the schedule).  Reports the
+    time of each schedule (interleaved A/B in one process), TFLOP/s, and the Linear-2 store
+    spans from the per-wave stamps (end of the k loop to the last store issued)."""
+    import numpy as np
+
+    from synth import MOE_WORKLOADS, moe_routing
+
+    w = MOE_WORKLOADS["moe_dsv3"]
+    offsets, dst_slab, dst_row, out_rows = moe_routing(w)
+    T = int(offsets[-1])
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    x = torch.randn((T, w.d_model), generator=g, device="cuda").to(torch.bfloat16)
+    w1 = (torch.randn((w.E, w.d_ff, w.d_model), generator=g, device="cuda") / math.sqrt(w.d_model)).to(torch.bfloat16)
+    w2 = (torch.randn((w.E, w.d_model, w.d_ff), generator=g, device="cuda") / math.sqrt(w.d_ff)).to(torch.bfloat16)
+    h = torch.empty((T, w.d_ff), dtype=torch.bfloat16, device="cuda")
+    outs = [torch.empty((int(r), w.d_model), dtype=torch.bfloat16, device="cuda") for r in out_rows]
+    ds = torch.from_numpy(dst_slab).cuda()
+    dr = torch.from_numpy(dst_row).cuda()
+    offs = [int(o) for o in offsets]
+    runs = [xs.bind("xstage_moe_waves_run", x, w1, w2, h, offs, ds, dr, outs, w.experts_per_wave, sch)
+            for sch in (0, 1)]
+    steps = max(5, min(args.steps, 50))
+    ms = {0: [], 1: []}
+    for rep in range(3):
+        for sch in (0, 1):
+            ms[sch].append(timed(runs[sch], steps, max(3, args.warmup // 20), torch))
+    flops = w.flops_per_token * T
+    res = {"workload": f"{w.name}: E={w.E} experts in waves of {w.experts_per_wave}, T={T} token rows "
+                       f"({w.rows_lo}-{w.rows_hi} per expert), d_model={w.d_model}, d_ff={w.d_ff}, P={w.P}",
+           "flop_per_layer": flops, "steps": steps}
+    spans = {}
+    for sch in (0, 1):
+        _, _, nl, nt = xs.xstage_moe_waves_plan(offs, w.d_model, w.d_ff, w.experts_per_wave, sch)
+        stamps = torch.zeros(nt * 16, dtype=torch.int64, device="cuda")
+        xs.xstage_moe_waves_run(x, w1, w2, h, offs, ds, dr, outs, w.experts_per_wave, sch, stamps=stamps)
+        torch.cuda.synchronize()
+        st = stamps.cpu().numpy().reshape(nt, 4, 4)
+        l2 = st[:, 0, 3] == 1
+        hz = xs.xstage_wallclock_hz()
+        span = (st[l2][:, :, 2] - st[l2][:, :, 1]).ravel() / hz * 1e6
+        spans[sch] = {"launches": nl, "l2_store_span_us_median": round(float(np.median(span)), 3),
+                      "l2_store_span_us_p90": round(float(np.percentile(span, 90)), 3)}
+        m = float(np.median(ms[sch]))
+        name = "expert_waves" if sch == 0 else "interleaved"
+        res[name] = {"ms": m, "TFLOPs": round(flops / (m * 1e-3) / 1e12, 2), **spans[sch]}
+    res["interleaved_speedup"] = round(float(np.median(ms[0])) / float(np.median(ms[1])), 4)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -268,6 +322,9 @@ def main():
         from attention_ulysses_a2a_amd.xstage_study import run_study
 
         run_study(torch, xs, emit=lambda line: print(line, flush=True))
+        return
+    if args.moe:
+        print(json.dumps(bench_moe(args, torch, xs)), flush=True)
         return
     if args.copy_calibration:
         # B=1, S=262144, H=8, D=128, P=8: 512 MiB read and 512 MiB written per call; the

@@ -165,6 +165,61 @@ int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void
                                int B, int S, int H_local, int D, int P, float scale, int mode,
                                unsigned long long* stamps, void* stream);
 
+/* Expert-wave grouped GEMM with the combine all-to-all in the Linear-2 epilogue: the
+ * stand-in for the interleaved scheduling of "Contributions", MegaMoE (reshaping) item, and
+ * "Results", MegaMoE optimisation.  E experts on this GPU; expert e owns the token rows
+ * [expert_offsets[e], expert_offsets[e+1]) of x and h (T = expert_offsets[E] tokens):
+ *   Linear-1:  h[t, :] = bf16(x[t, :] . w1[e]^T)            (h: [T, d_ff], written)
+ *   Linear-2:  y[t, :] = bf16(h[t, :] . w2[e]^T), stored to out[dst_slab[t]][dst_row[t], :]
+ * with fp32 accumulation and round-to-nearest-even bf16 results; no activation between the
+ * two products.  Experts are grouped into waves of experts_per_wave in index order.
+ *   schedule 0 (expert waves): per wave, one launch of its Linear-1 tiles, then one of its
+ *              Linear-2 tiles (the stores of a wave come in one concentrated phase);
+ *   schedule 1 (interleaved): Linear-1 of wave 0, then for every wave w one launch mixing
+ *              the Linear-2 tiles of wave w with the Linear-1 tiles of wave w+1 (the
+ *              Linear-1 tiles are dispatched first; Linear-2 tiles run beside them).
+ * Both schedules give the same result bit for bit.  Layouts (bf16, row-major):
+ *   x [T, d_model], w1 [E, d_ff, d_model], w2 [E, d_model, d_ff] (weights as a linear
+ *   layer stores them: output features by input features), h [T, d_ff] (caller-owned
+ *   workspace), out[p] [out_rows[p], d_model]; dst_slab, dst_row: device int32 [T].
+ * A token whose (dst_slab, dst_row) is outside [0, P) x [0, out_rows[p]) is not stored.
+ *   stamps (optional, NULL for none): device uint64 [n_tiles][4 waves][4] (n_tiles from
+ *   xstage_moe_waves_plan: all Linear-1 tiles in expert order, then all Linear-2 tiles) in
+ *   wall-clock ticks: start, end of the k loop, last store issued, then the tile type (0, 1).
+ * Requires 1 <= E <= 4096, d_model and d_ff multiples of 128 (<= 65536),
+ * 1 <= experts_per_wave <= 32, schedule in {0, 1}, expert_offsets (HOST, E + 1 entries)
+ * starting at 0 and nondecreasing, 1 <= P <= XSTAGE_MAX_P, out_rows[p] >= 0, 16-byte
+ * aligned bf16 pointers, 4-byte aligned index arrays; h, every out[p] and stamps must not
+ * overlap each other or any input.  Else XSTAGE_ERR_INVALID / XSTAGE_ERR_UNSUPPORTED. */
+typedef struct {
+  int E;
+  int d_model;
+  int d_ff;
+  int experts_per_wave;
+  int schedule;
+  const int* expert_offsets;
+  const void* x;
+  const void* w1;
+  const void* w2;
+  void* h;
+  const int* dst_slab;
+  const int* dst_row;
+  int P;
+  void* const* out;
+  const int* out_rows;
+  unsigned long long* stamps;
+} xstage_moe_params_t;
+
+int xstage_moe_waves_run(const xstage_moe_params_t* p, void* stream);
+
+/* The launches of a schedule, host only: for every expert e, l1_launch[e] and l2_launch[e]
+ * are the indices of the launches holding its Linear-1 and Linear-2 tiles; *n_launches the
+ * number of launches, *n_tiles the tiles of both kinds (sizes the stamps).  Arrays hold at
+ * least E ints (caller-owned).  Same requirements on the shape as xstage_moe_waves_run. */
+int xstage_moe_waves_plan(int E, const int* expert_offsets, int d_model, int d_ff,
+                          int experts_per_wave, int schedule, int* l1_launch, int* l2_launch,
+                          int* n_launches, int* n_tiles);
+
 /* Burst-Gap store microbenchmark ("Methodology"; "Contributions", characterisation item).
  * K producer workgroups (256 threads each) run `rounds` rounds of: a burst that stores
  * V_bytes / K bytes as 16-byte stores into the producer's share of destination set

@@ -17,6 +17,8 @@ Inference", technical summary):
 * ``ulysses``: the pre-attention (sequence -> heads) and post-attention (heads -> sequence)
   all-to-alls of one rank of a Ulysses group, with full-head shards and receive buffers,
   as plain loops, and one rank's attention layer built from them.
+* ``moe``: the mixture-of-experts layer of the expert-wave stand-in (Linear-1, bf16
+  intermediate, Linear-2, then the combine all-to-all's row placement) in float64.
 * ``burst_gap``: the Burst-Gap issue-time model of the "Methodology" section,
   T_iss(G; K, V) = max(T0_iss(K, V), V / R - G), its two regimes, a labelled fluid-queue
   reading that gives the capacity Q a role, and the parameter fit used on microbenchmark
@@ -38,6 +40,7 @@ from .attention import (  # noqa: F401
     ulysses_scatter,
 )
 from .ulysses import pre_gather, scatter_heads, ulysses_attention  # noqa: F401
+from .moe import moe_layer  # noqa: F401
 from .burst_gap import (  # noqa: F401
     fit_burst_gap,
     regime,

@@ -47,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -327,3 +327,75 @@ def test_xcd_unit_order_is_a_bijection():
             assert 0 <= L < n
             seen.add(L)
         assert len(seen) == n
+
+
+# ---- expert-wave stand-in: schedule plan (host) and argument checks -----------------------
+MOE_OFFS = [0, 90, 90, 300, 301, 700]  # 5 experts, one with no tokens
+
+
+@pytest.mark.parametrize("epw", [1, 2, 3, 5, 8])
+def test_moe_plan_covers_every_expert_in_dependency_order(L, epw):
+    E = len(MOE_OFFS) - 1
+    waves = [list(range(w, min(E, w + epw))) for w in range(0, E, epw)]
+    l1a, l2a, na, nta = xs.xstage_moe_waves_plan(MOE_OFFS, 256, 128, epw, 0)
+    l1b, l2b, nb, ntb = xs.xstage_moe_waves_plan(MOE_OFFS, 256, 128, epw, 1)
+    rows = [MOE_OFFS[e + 1] - MOE_OFFS[e] for e in range(E)]
+    tiles = sum(-(-r // 128) * (128 // 128 + 256 // 128) for r in rows)
+    assert nta == ntb == tiles
+    assert na == 2 * len(waves) and nb == len(waves) + 1
+    for wi, wave in enumerate(waves):
+        for e in wave:
+            assert (l1a[e], l2a[e]) == (2 * wi, 2 * wi + 1)   # expert waves: L1(w), then L2(w)
+            assert (l1b[e], l2b[e]) == (wi, wi + 1)           # interleaved: L2(w) with L1(w+1)
+            assert l2a[e] > l1a[e] and l2b[e] > l1b[e]
+    # the interleaved launches hold Linear-2 of wave w together with Linear-1 of wave w+1
+    for wi in range(len(waves) - 1):
+        assert {l2b[e] for e in waves[wi]} == {l1b[e] for e in waves[wi + 1]}
+
+
+@no_device
+def test_moe_rejects(L):
+    import ctypes
+
+    def run(**kw):
+        offs = kw.pop("offs", MOE_OFFS)
+        T = offs[-1]
+        base = dict(E=len(offs) - 1, d_model=256, d_ff=128, experts_per_wave=2, schedule=0, x=0x10_0000_0000,
+                    w1=0x20_0000_0000, w2=0x30_0000_0000, h=0x40_0000_0000, dst_slab=0x50_0000_0000,
+                    dst_row=0x50_1000_0000, P=2, stamps=None)
+        outs = kw.pop("outs", [0x60_0000_0000, 0x70_0000_0000])
+        rows = kw.pop("rows", [T, T])
+        base.update(kw)
+        oarr, keep = _lib.ptr_array(outs)
+        prm = _lib.MoeParams(base["E"], base["d_model"], base["d_ff"], base["experts_per_wave"], base["schedule"],
+                             (ctypes.c_int * len(offs))(*offs), base["x"], base["w1"], base["w2"], base["h"],
+                             base["dst_slab"], base["dst_row"], base["P"], oarr, (ctypes.c_int * max(1, len(rows)))(*rows),
+                             base["stamps"])
+        return L.xstage_moe_waves_run(ctypes.byref(prm), None)
+
+    assert L.xstage_moe_waves_run(None, None) == INVALID
+    assert run(E=0) == INVALID
+    assert run(d_model=200) == INVALID            # not a multiple of 128
+    assert run(d_ff=0) == INVALID
+    assert run(experts_per_wave=0) == INVALID
+    assert run(experts_per_wave=33) == UNSUPPORTED
+    assert run(schedule=2) == INVALID
+    assert run(offs=[1, 90, 300, 301, 700, 700]) == INVALID   # must start at 0
+    assert run(offs=[0, 90, 80, 301, 700, 700]) == INVALID    # decreasing
+    assert run(x=0) == INVALID
+    assert run(w2=0x30_0000_0008) == INVALID     # misaligned
+    assert run(dst_row=0x50_1000_0002) == INVALID
+    assert run(P=0) == INVALID
+    assert run(P=65) == UNSUPPORTED
+    assert run(outs=[0x60_0000_0000, 0]) == INVALID
+    assert run(rows=[700, -1]) == INVALID
+    assert run(h=0x10_0000_0000 + 256) == INVALID                 # h overlaps x
+    assert run(outs=[0x60_0000_0000, 0x60_0000_0000 + 512]) == INVALID  # outputs overlap
+    assert run(outs=[0x60_0000_0000, 0x20_0000_0000]) == INVALID  # an output overlaps w1
+    assert run(stamps=0x80_0000_0004) == INVALID   # misaligned stamps
+    assert run(stamps=0x40_0000_0000) == INVALID   # stamps overlap h
+    n = _lib.ctypes.c_int(0)
+    arr = (_lib.ctypes.c_int * 8)()
+    offs = (_lib.ctypes.c_int * 6)(*MOE_OFFS)
+    assert L.xstage_moe_waves_plan(5, offs, 256, 128, 2, 0, None, arr, _lib.ctypes.byref(n), _lib.ctypes.byref(n)) == INVALID
+    assert L.xstage_moe_waves_plan(5, offs, 256, 100, 2, 0, arr, arr, _lib.ctypes.byref(n), _lib.ctypes.byref(n)) == INVALID
