@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--bg", action="store_true", help="run the Burst-Gap store sweep instead")
     ap.add_argument("--xstage-study", action="store_true",
                     help="fused-epilogue overhead and store spans against sequence length (one JSON line per S)")
+    ap.add_argument("--profile-launches", type=int, default=0,
+                    help="only issue this many fused launches of the workload (for counter collection)")
     ap.add_argument("--moe", action="store_true",
                     help="expert-wave grouped-GEMM stand-in: expert waves vs interleaved schedule")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -325,6 +327,21 @@ def main():
         return
     if args.moe:
         print(json.dumps(bench_moe(args, torch, xs)), flush=True)
+        return
+    if args.profile_launches > 0:
+        import numpy as np
+
+        from synth import make_inputs, workload
+
+        w = workload(args.workload)
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).cuda().view(torch.bfloat16)
+                   for b in make_inputs(w))
+        slabs = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+        fused = xs.bind("xstage_attn_a2a_fwd", q, k, v, [slabs[p] for p in range(w.P)], w.scale)
+        for _ in range(args.profile_launches):
+            fused()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_launches": args.profile_launches, "workload": w.name}), flush=True)
         return
     if args.copy_calibration:
         # B=1, S=262144, H=8, D=128, P=8: 512 MiB read and 512 MiB written per call; the
