@@ -45,6 +45,7 @@ __all__ = [
     "xstage_burst_gap_run",
     "xstage_wallclock_hz",
     "xstage_bg_t_iss",
+    "xstage_bg_pacing_chunks",
     "xstage_status_str",
     "bind",
     "LibraryMissing",
@@ -345,6 +346,16 @@ def xstage_wallclock_hz() -> float:
 
 def xstage_bg_t_iss(G_s: float, T0_s: float, V_bytes: float, R_bytes_per_s: float) -> float:
     return lib().xstage_bg_t_iss(float(G_s), float(T0_s), float(V_bytes), float(R_bytes_per_s))
+
+
+def xstage_bg_pacing_chunks(V_bytes, G_s, a_s, f1_Bps, R_Bps, Q_bytes, c_max=64):
+    """(c, issuer-visible seconds) of the Burst-Gap pacing choice; see include/xstage.h."""
+    t = ctypes.c_double(0.0)
+    c = lib().xstage_bg_pacing_chunks(float(V_bytes), float(G_s), float(a_s), float(f1_Bps), float(R_Bps),
+                                      float(Q_bytes), int(c_max), ctypes.byref(t))
+    if c < 1:
+        raise ValueError("xstage_bg_pacing_chunks: invalid parameters")
+    return c, t.value
 
 
 def xstage_status_str(status: int) -> str:

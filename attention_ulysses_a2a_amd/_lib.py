@@ -85,6 +85,7 @@ SIGNATURES = {
     "xstage_burst_gap_run": (_i, [ctypes.POINTER(BGParams), _vp]),
     "xstage_wallclock_hz": (_i, [ctypes.POINTER(ctypes.c_double)]),
     "xstage_bg_t_iss": (ctypes.c_double, [ctypes.c_double] * 4),
+    "xstage_bg_pacing_chunks": (_i, [ctypes.c_double] * 6 + [_i, ctypes.POINTER(ctypes.c_double)]),
     "xstage_status_str": (ctypes.c_char_p, [_i]),
 }
 

@@ -91,6 +91,14 @@ def run_sweep(torch, xs, out=print, variants=("hot", "cold")):
                     out(json.dumps({"bg": rec}))
                     pts.append((K, V, g * 1e-6, m["T_iss_us"] * 1e-6))
         f = fit(pts)
+        cap = f.get("capacity_reading")
+        if cap:
+            # The attention epilogue's burst: one workgroup's output tile (128 rows x 128 x 2 B)
+            # from one producer; with no compute after it (G = 0) the chooser gives the chunk
+            # count that no following tile could lower.
+            tile = 128 * 128 * 2
+            c, t = xs.xstage_bg_pacing_chunks(tile, 0.0, cap["c_s"], cap["f1_Bps"], cap["R_Bps"], cap["Q_bytes"])
+            f["pacing_attention_tile"] = {"tile_bytes": tile, "G_us": 0.0, "chunks": c, "T_visible_us": t * 1e6}
         summary[variant] = f
         out(json.dumps({"bg_fit": {"variant": variant, **{k: v for k, v in f.items() if k != "T0"},
                                    "T0_us": {k: v * 1e6 for k, v in f["T0"].items()}}}))

@@ -293,6 +293,28 @@ double xstage_bg_t_iss(double G_s, double T0_s, double V_bytes, double R_bytes_p
   return drain > T0_s ? drain : T0_s;
 }
 
+int xstage_bg_pacing_chunks(double V_bytes, double G_s, double a_s, double f1_Bps, double R_Bps, double Q_bytes,
+                            int c_max, double* t_visible_s) {
+  const double in[6] = {V_bytes, G_s, a_s, f1_Bps, R_Bps, Q_bytes};
+  for (double x : in)
+    if (!isfinite(x) || x < 0) return 0;
+  if (!(R_Bps > 0) || !(f1_Bps > 0) || c_max < 1) return 0;
+  int best = 1;
+  double best_t = 0.0;
+  for (int c = 1; c <= c_max; ++c) {
+    const double issue = c * a_s + V_bytes / f1_Bps;
+    const double hidden = G_s < c * Q_bytes / R_Bps ? G_s : c * Q_bytes / R_Bps;
+    const double drain = V_bytes / R_Bps - hidden;
+    const double t = issue > drain ? issue : drain;
+    if (c == 1 || t < best_t) {
+      best = c;
+      best_t = t;
+    }
+  }
+  if (t_visible_s) *t_visible_s = best_t;
+  return best;
+}
+
 const char* xstage_status_str(int status) {
   switch (status) {
     case XSTAGE_OK: return "XSTAGE_OK";

@@ -256,6 +256,19 @@ int xstage_wallclock_hz(double* hz);
  * in bytes per second.  Returns a negative value for R <= 0 or non-finite inputs. */
 double xstage_bg_t_iss(double G_s, double T0_s, double V_bytes, double R_bytes_per_s);
 
+/* Pacing chunk count for an epilogue burst, host only: the Burst-Gap model ("Methodology")
+ * applied to a tile of V_bytes that a producer issues before the G_s seconds of compute of
+ * its next tile, with the capacity reading of the printed formula (pending capacity
+ * Q_bytes drained at R; issue time without backpressure a_s + V / f1_Bps for a burst of V).
+ * Issuing the tile as c chunks of V/c, each followed by G/c of the compute, lets every
+ * chunk use the whole capacity, so the tile's issuer-visible time is
+ *   T(c) = max(c * a + V / f1, V / R - min(G, c * Q / R)).
+ * Returns the smallest c in [1, c_max] minimising T(c), and T(c) in *t_visible_s (may be
+ * NULL); c = 1 is the unpaced burst.  Returns 0 for non-finite or negative inputs,
+ * R <= 0, f1 <= 0 or c_max < 1. */
+int xstage_bg_pacing_chunks(double V_bytes, double G_s, double a_s, double f1_Bps, double R_Bps, double Q_bytes,
+                            int c_max, double* t_visible_s);
+
 /* Static string naming a status code. */
 const char* xstage_status_str(int status);
 

@@ -44,3 +44,47 @@ def test_library_formula_matches_oracle():
     assert np.allclose(got, oracle.t_iss(G, 10e-6, 64 * 2 ** 20, 717e9), rtol=0, atol=1e-15)
     got_q = bg_model.t_iss_capacity(G, 10e-6, 64 * 2 ** 20, 717e9, 8 * 2 ** 20)
     assert np.allclose(got_q, oracle.t_iss_fluid(G, 10e-6, 64 * 2 ** 20, 717e9, 8 * 2 ** 20), rtol=0, atol=1e-15)
+
+
+def test_pacing_chunks_hand_values():
+    """T(c) = max(c a + V/f1, V/R - min(G, c Q/R)), smallest c minimising it.
+
+    Remote-like burst, with the pages' printed drain rate: V = 64 MiB, R = 717 GB/s,
+    Q = 8 MiB, G = 50 us, a = 1 us, f1 = 1e12 B/s.  By hand (us): V/R = 93.5967,
+    Q/R = 11.6996, V/f1 = 67.1089;  c=1: max(68.1089, 81.8971) = 81.8971;
+    c=2: max(69.1089, 70.1975) = 70.1975;  c=3: max(70.1089, 58.4979) = 70.1089;
+    c=4: max(71.1089, 46.7983) = 71.1089 -> c = 3, 70.1089 us."""
+    import attention_ulysses_a2a_amd as xs
+
+    c, t = xs.xstage_bg_pacing_chunks(64 * 2**20, 50e-6, 1e-6, 1e12, 717e9, 8 * 2**20, c_max=16)
+    assert c == 3
+    assert abs(t - 70.1089e-6) < 1e-10
+    c, t = xs.xstage_bg_pacing_chunks(64 * 2**20, 50e-6, 1e-6, 1e12, 717e9, 8 * 2**20, c_max=2)
+    assert c == 2 and abs(t - 70.1975e-6) < 1e-10
+    c, t = xs.xstage_bg_pacing_chunks(64 * 2**20, 50e-6, 1e-6, 1e12, 717e9, 8 * 2**20, c_max=1)
+    assert c == 1 and abs(t - 81.8971e-6) < 1e-10
+
+
+def test_pacing_chunks_local_tile_is_unpaced():
+    """A FLUX-1024 output tile (128 rows x 128 x 2 B = 32 KiB) at the local parameters fitted
+    on MI355X (R 7.55 TB/s, Q 113 MiB, f1 131 GB/s; a = 1 us assumed, G = 30 us of key loop):
+    c=1 gives max(1 us + 0.250 us, 4.3 ns - 15.7 us) = 1.250 us and every extra chunk adds a,
+    so the tile goes out as one burst."""
+    import attention_ulysses_a2a_amd as xs
+
+    c, t = xs.xstage_bg_pacing_chunks(32768, 30e-6, 1e-6, 131e9, 7.55e12, 113 * 2**20)
+    assert c == 1 and abs(t - (1e-6 + 32768 / 131e9)) < 1e-12
+    # no fixed cost and no backpressure: every c ties, the smallest wins
+    assert xs.xstage_bg_pacing_chunks(32768, 30e-6, 0.0, 131e9, 7.55e12, 113 * 2**20)[0] == 1
+
+
+def test_pacing_chunks_rejects():
+    from attention_ulysses_a2a_amd import _lib
+
+    L = _lib.lib()
+    assert L.xstage_bg_pacing_chunks(1.0, 1.0, 1.0, 1.0, 0.0, 1.0, 4, None) == 0      # R = 0
+    assert L.xstage_bg_pacing_chunks(1.0, 1.0, 1.0, 0.0, 1.0, 1.0, 4, None) == 0      # f1 = 0
+    assert L.xstage_bg_pacing_chunks(1.0, -1.0, 1.0, 1.0, 1.0, 1.0, 4, None) == 0     # G < 0
+    assert L.xstage_bg_pacing_chunks(float("nan"), 1.0, 1.0, 1.0, 1.0, 1.0, 4, None) == 0
+    assert L.xstage_bg_pacing_chunks(1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 0, None) == 0      # c_max < 1
+    assert L.xstage_bg_pacing_chunks(1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1, None) == 1
