@@ -67,7 +67,7 @@ def test_pacing_chunks_hand_values():
 
 def test_pacing_chunks_local_tile_is_unpaced():
     """A FLUX-1024 output tile (128 rows x 128 x 2 B = 32 KiB) at the local parameters fitted
-    on MI355X (R 7.55 TB/s, Q 113 MiB, f1 131 GB/s; a = 1 us assumed, G = 30 us of key loop):
+    on MI355X in one sweep (R 7.55 TB/s, Q 113 MiB, f1 131 GB/s; a = 1 us assumed, G = 30 us of key loop):
     c=1 gives max(1 us + 0.250 us, 4.3 ns - 15.7 us) = 1.250 us and every extra chunk adds a,
     so the tile goes out as one burst."""
     import attention_ulysses_a2a_amd as xs
