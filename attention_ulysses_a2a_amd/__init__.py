@@ -37,6 +37,9 @@ __all__ = [
     "xstage_attn_a2a_unfused",
     "xstage_attn_a2a_fwd_strided",
     "xstage_ulysses_attn_fwd",
+    "xstage_ulysses_gather",
+    "xstage_a2a_scatter_strided",
+    "xstage_ulysses_attn_unfused",
     "xstage_attn_a2a_plan",
     "xstage_attn_a2a_schedule",
     "xstage_attn_a2a_fwd_traced",
@@ -137,6 +140,58 @@ def _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream):
     call = (arrs[0][0], arrs[1][0], arrs[2][0], arrs[3][0], B, sp * P, H, int(H_local), int(h0), D, P,
             _scale(scale, D), _stream_of(t0, stream))
     return call, [a[1] for a in arrs], t0.device
+
+
+def xstage_ulysses_gather(src_shards, out, H_local, h0, stream=None) -> None:
+    """Pre-attention all-to-all as a separate copy: heads [h0, h0 + H_local) of the P sequence
+    shards into the contiguous out [B, S, H_local, D]; see include/xstage.h."""
+    import torch
+
+    ptrs, (B, sp, H, D) = _shards(src_shards, "src_shards")
+    _dev_tensor(out, "out")
+    P = len(ptrs)
+    arr, keep = ptr_array(ptrs)
+    with torch.cuda.device(out.device):
+        st = lib().xstage_ulysses_gather(arr, out.data_ptr(), B, sp * P, H, int(H_local), int(h0), D, P,
+                                         _stream_of(out, stream))
+    del keep
+    _check(st, "xstage_ulysses_gather")
+
+
+def xstage_a2a_scatter_strided(inp, out_dst, h_dst0, stream=None) -> None:
+    """Post-attention all-to-all as a separate copy into full-head receive buffers."""
+    import torch
+
+    _dev_tensor(inp, "in")
+    B, S, H, D = (int(x) for x in inp.shape)
+    ptrs, shp = _shards(out_dst, "out_dst")
+    P = len(ptrs)
+    arr, keep = ptr_array(ptrs)
+    with torch.cuda.device(inp.device):
+        st = lib().xstage_a2a_scatter_strided(inp.data_ptr(), arr, B, S, H, D, P, shp[2], int(h_dst0),
+                                              _stream_of(inp, stream))
+    del keep
+    _check(st, "xstage_a2a_scatter_strided")
+
+
+def _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream):
+    call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
+    _dev_tensor(workspace, "workspace")
+    # (q, k, v, out, B, S, H, H_local, h0, D, P, scale, stream) -> insert the workspace
+    call = call[:3] + (workspace.data_ptr(),) + call[3:]
+    return call, keep + [workspace], dev
+
+
+def xstage_ulysses_attn_unfused(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=None, stream=None) -> None:
+    """Serial Ulysses layer: separate gather, attention, separate strided scatter;
+    ``workspace`` holds 4 x [B, S, H_local, D] bf16."""
+    import torch
+
+    call, keep, dev = _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream)
+    with torch.cuda.device(dev):
+        st = lib().xstage_ulysses_attn_unfused(*call)
+    del keep
+    _check(st, "xstage_ulysses_attn_unfused")
 
 
 def xstage_attn_a2a_fwd_strided(q, k, v, out_dst, h_dst0, scale=None, stream=None) -> None:
@@ -386,8 +441,8 @@ def bind(name: str, *args, **kwargs) -> _Bound:
     current stream of the tensors' device unless ``stream`` is given), and the calls must be
     made with that device current.  Supported: xstage_attn_a2a_fwd, xstage_attn_fwd,
     xstage_a2a_scatter, xstage_attn_a2a_unfused, xstage_attn_a2a_fwd_traced,
-    xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd, xstage_moe_waves_run, with the same
-    arguments as the functions.
+    xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd, xstage_ulysses_attn_unfused,
+    xstage_moe_waves_run, with the same arguments as the functions.
     """
     import torch
 
@@ -446,6 +501,11 @@ def bind(name: str, *args, **kwargs) -> _Bound:
         scale, stream = kwargs.get("scale", args[6] if len(args) > 6 else None), kwargs.get("stream")
         call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
         refs = (q_src, k_src, v_src, out_dst, keep)
+    elif name == "xstage_ulysses_attn_unfused":
+        q_src, k_src, v_src, workspace, out_dst, H_local, h0 = args[:7]
+        scale, stream = kwargs.get("scale", args[7] if len(args) > 7 else None), kwargs.get("stream")
+        call, keep, dev = _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream)
+        refs = (q_src, k_src, v_src, workspace, out_dst, keep)
     elif name == "xstage_moe_waves_run":
         x, w1, w2, h, expert_offsets, dst_slab, dst_row, outs, epw, schedule = args[:10]
         stamps, stream = kwargs.get("stamps", args[10] if len(args) > 10 else None), kwargs.get("stream")

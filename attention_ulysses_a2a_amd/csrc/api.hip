@@ -17,6 +17,9 @@ int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable
 int attn_workgroups(int B, int S, int H, int D, int* n_split);
 int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, int* j0, int* j1);
 int launch_scatter(const void* in, const SlabTable& slabs, int B, int S, int H, int D, int P, hipStream_t stream);
+int launch_slice_copy(const void* const* src, int src_sharded, int src_w, int src_off, void* const* dst,
+                      int dst_sharded, int dst_w, int dst_off, int B, int S, int H_local, int D, int P,
+                      hipStream_t stream);
 int launch_burst_gap(const xstage_bg_params_t& p, hipStream_t stream);
 
 static SlabTable make_table(void* const* slabs, int P) {
@@ -138,6 +141,92 @@ int xstage_ulysses_attn_fwd(const void* const* q_src, const void* const* k_src, 
   lay.dst_head0 = h0;
   return launch_attn_any(q_src[0], k_src[0], v_src[0], make_table(out_dst, P), B, S, H_local, D, P, scale,
                          static_cast<hipStream_t>(stream), 0, nullptr, &lay);
+}
+
+// Shared checks of the Ulysses layouts: P shard pointers (non-null, aligned) of
+// B*S*H*D*2/P bytes each, collected into `ranges`.
+static int collect_shards(const void* const* shards, int P, unsigned long long bytes, std::vector<Range>* ranges) {
+  if (shards == nullptr) return XSTAGE_ERR_INVALID;
+  for (int p = 0; p < P; ++p) {
+    if (shards[p] == nullptr || !aligned16(shards[p])) return XSTAGE_ERR_INVALID;
+    ranges->push_back(range_of(shards[p], bytes));
+  }
+  return XSTAGE_OK;
+}
+
+static bool disjoint_from(Range r, const std::vector<Range>& others) {
+  for (const Range& o : others)
+    if (overlaps(r, o)) return false;
+  return true;
+}
+
+int xstage_ulysses_gather(const void* const* src_shards, void* out, int B, int S, int H, int H_local, int h0, int D,
+                          int P, void* stream) {
+  int st = check_shape(B, S, H, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (H_local <= 0 || H_local > H || h0 < 0 || h0 > H - H_local) return XSTAGE_ERR_INVALID;
+  if (out == nullptr || !aligned16(out)) return XSTAGE_ERR_INVALID;
+  std::vector<Range> src;
+  st = collect_shards(src_shards, P, tensor_bytes(B, S, H, D) / (unsigned long long)P, &src);
+  if (st != XSTAGE_OK) return st;
+  if (!disjoint_from(range_of(out, tensor_bytes(B, S, H_local, D)), src)) return XSTAGE_ERR_INVALID;
+  void* dst[1] = {out};
+  return launch_slice_copy(src_shards, 1, H * D, h0 * D, dst, 0, H_local * D, 0, B, S, H_local, D, P,
+                           static_cast<hipStream_t>(stream));
+}
+
+int xstage_a2a_scatter_strided(const void* in, void* const* out_dst, int B, int S, int H_local, int D, int P, int H_dst,
+                               int h_dst0, void* stream) {
+  int st = check_shape(B, S, H_local, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (H_dst < H_local || h_dst0 < 0 || h_dst0 > H_dst - H_local) return XSTAGE_ERR_INVALID;
+  st = check_shape(B, S, H_dst, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (in == nullptr || !aligned16(in)) return XSTAGE_ERR_INVALID;
+  const Range others[1] = {range_of(in, tensor_bytes(B, S, H_local, D))};
+  st = check_slabs(out_dst, P, tensor_bytes(B, S, H_dst, D) / (unsigned long long)P, others, 1);
+  if (st != XSTAGE_OK) return st;
+  const void* src[1] = {in};
+  return launch_slice_copy(src, 0, H_local * D, 0, out_dst, 1, H_dst * D, h_dst0 * D, B, S, H_local, D, P,
+                           static_cast<hipStream_t>(stream));
+}
+
+int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_src, const void* const* v_src,
+                                void* workspace, void* const* out_dst, int B, int S, int H, int H_local, int h0,
+                                int D, int P, float scale, void* stream) {
+  int st = check_shape(B, S, H, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (H_local <= 0 || H_local > H || h0 < 0 || h0 > H - H_local) return XSTAGE_ERR_INVALID;
+  if (workspace == nullptr || !aligned16(workspace) || !std::isfinite(scale)) return XSTAGE_ERR_INVALID;
+  const unsigned long long shard = tensor_bytes(B, S, H, D) / (unsigned long long)P;
+  const unsigned long long tl = tensor_bytes(B, S, H_local, D);
+  std::vector<Range> src;
+  for (const void* const* t : {q_src, k_src, v_src}) {
+    st = collect_shards(t, P, shard, &src);
+    if (st != XSTAGE_OK) return st;
+  }
+  const Range ws = range_of(workspace, 4 * tl);
+  if (!disjoint_from(ws, src)) return XSTAGE_ERR_INVALID;
+  std::vector<Range> others = src;
+  others.push_back(ws);
+  st = check_slabs(out_dst, P, shard, others.data(), (int)others.size());
+  if (st != XSTAGE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  void* qc[1] = {w};
+  void* kc[1] = {w + tl};
+  void* vc[1] = {w + 2 * tl};
+  void* oc[1] = {w + 3 * tl};
+  for (int i = 0; i < 3; ++i) {
+    const void* const* srcs = i == 0 ? q_src : i == 1 ? k_src : v_src;
+    void* const* dst = i == 0 ? qc : i == 1 ? kc : vc;
+    st = launch_slice_copy(srcs, 1, H * D, h0 * D, dst, 0, H_local * D, 0, B, S, H_local, D, P, s);
+    if (st != XSTAGE_OK) return st;
+  }
+  st = launch_attn_any(qc[0], kc[0], vc[0], make_table(oc, 1), B, S, H_local, D, 1, scale, s);
+  if (st != XSTAGE_OK) return st;
+  const void* osrc[1] = {oc[0]};
+  return launch_slice_copy(osrc, 0, H_local * D, 0, out_dst, 1, H * D, h0 * D, B, S, H_local, D, P, s);
 }
 
 int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_split) {

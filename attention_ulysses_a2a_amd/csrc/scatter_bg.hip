@@ -59,6 +59,74 @@ int launch_scatter(const void* in, const SlabTable& slabs, int B, int S, int H, 
 }
 
 // ---------------------------------------------------------------------------------------
+// Head-slice copy: the two all-to-alls of a Ulysses layer as separate steps.  Every row of
+// the B x S sequence carries a slice of H_local * D elements at an offset within a row of
+// src_w (resp. dst_w) elements; a side is either one contiguous tensor of S rows or P
+// sequence shards of S/P rows each (row s in shard s / (S/P)).  Pre-attention: shards of all
+// heads -> a contiguous local-head tensor; post-attention: the reverse into full-head
+// receive buffers.  Each thread moves 4 chunks of 16 bytes.
+struct SliceCopyArgs {
+  const uint16_t* src[XSTAGE_MAX_P];
+  uint16_t* dst[XSTAGE_MAX_P];
+  int src_sharded, dst_sharded;
+  uint32_t S, src_rows, dst_rows;
+  uint32_t src_w, dst_w, src_off, dst_off;
+  uint32_t row_chunks;
+  uint32_t total_chunks;
+};
+
+__global__ __launch_bounds__(256) void slice_copy_kernel(const SliceCopyArgs a) {
+  // B * S * H_local * D < 2^31 elements (checked on the host), so chunk and row indices fit
+  // 32 bits.
+  const uint32_t base = blockIdx.x * (kScatterThreads * kScatterUnroll) + threadIdx.x;
+  u32x4 r[kScatterUnroll];
+  u32x4* dp[kScatterUnroll];
+#pragma unroll
+  for (int i = 0; i < kScatterUnroll; ++i) {
+    const uint32_t g = base + i * kScatterThreads;
+    dp[i] = nullptr;
+    if (g < a.total_chunks) {
+      const uint32_t row = g / a.row_chunks;
+      const uint32_t ch = g - row * a.row_chunks;
+      const uint32_t b = row / a.S, s = row - b * a.S;
+      const uint32_t ps = a.src_sharded ? s / a.src_rows : 0, rs = s - ps * a.src_rows;
+      const uint32_t pd = a.dst_sharded ? s / a.dst_rows : 0, rd = s - pd * a.dst_rows;
+      const uint16_t* src = a.src[ps] + ((size_t)b * a.src_rows + rs) * a.src_w + a.src_off + (size_t)ch * 8;
+      dp[i] = reinterpret_cast<u32x4*>(a.dst[pd] + ((size_t)b * a.dst_rows + rd) * a.dst_w + a.dst_off + (size_t)ch * 8);
+      r[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kScatterUnroll; ++i)
+    if (dp[i]) *dp[i] = r[i];
+}
+
+int launch_slice_copy(const void* const* src, int src_sharded, int src_w, int src_off, void* const* dst,
+                      int dst_sharded, int dst_w, int dst_off, int B, int S, int H_local, int D, int P,
+                      hipStream_t stream) {
+  SliceCopyArgs a = {};
+  const int ns = src_sharded ? P : 1, nd = dst_sharded ? P : 1;
+  for (int i = 0; i < ns; ++i) a.src[i] = static_cast<const uint16_t*>(src[i]);
+  for (int i = 0; i < nd; ++i) a.dst[i] = static_cast<uint16_t*>(dst[i]);
+  a.src_sharded = src_sharded;
+  a.dst_sharded = dst_sharded;
+  a.S = (uint32_t)S;
+  a.src_rows = (uint32_t)(src_sharded ? S / P : S);
+  a.dst_rows = (uint32_t)(dst_sharded ? S / P : S);
+  a.src_w = (uint32_t)src_w;
+  a.dst_w = (uint32_t)dst_w;
+  a.src_off = (uint32_t)src_off;
+  a.dst_off = (uint32_t)dst_off;
+  a.row_chunks = (uint32_t)(H_local * D / 8);
+  a.total_chunks = (uint32_t)((unsigned long long)B * S * a.row_chunks);
+  const uint32_t per_block = kScatterThreads * kScatterUnroll;
+  const uint32_t blocks = (a.total_chunks + per_block - 1) / per_block;
+  if (blocks == 0) return XSTAGE_OK;
+  hipLaunchKernelGGL(slice_copy_kernel, dim3(blocks), dim3(kScatterThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------------------
 // Burst-Gap producer: K workgroups of 4 waves.  Per round: barrier, stamp, issue the burst
 // as 16-byte stores (nothing waits on them), barrier (every wave has issued), stamp, FMA
 // gap, stamp.  The barriers carry no memory fence, so they order issue, not completion.

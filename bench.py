@@ -179,9 +179,13 @@ def bench_attention(args, torch, xs):
                for _ in range(w.P)] for _ in range(3)]
     strided = xs.bind("xstage_attn_a2a_fwd_strided", q, k, v, recv, h0, w.scale)
     layer = xs.bind("xstage_ulysses_attn_fwd", shards[0], shards[1], shards[2], recv, w.H, h0, w.scale)
+    ws4 = torch.empty((4, w.B, w.S, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    layer_serial = xs.bind("xstage_ulysses_attn_unfused", shards[0], shards[1], shards[2], ws4, recv, w.H, h0,
+                           w.scale)
     ms_strided = timed(strided, args.steps, leg_warmup, torch)
     ms_layer = timed(layer, args.steps, leg_warmup, torch)
-    del shards, recv
+    ms_layer_serial = timed(layer_serial, args.steps, leg_warmup, torch)
+    del shards, recv, ws4
 
     # Core clock during the key loop (traced call, mode 3: shader-clock ticks against
     # wall-clock ticks per wave), right after back-to-back fused launches: the published
@@ -232,6 +236,8 @@ def bench_attention(args, torch, xs):
         "ms_ulysses_layer": ms_layer,
         "ulysses_layer_vs_fused": round(ms_layer / ms, 4),
         "ulysses_layer_TFLOPs": round(w.flops / (ms_layer * 1e-3) / 1e12, 3),
+        "ms_ulysses_layer_serial": ms_layer_serial,
+        "ulysses_fused_vs_serial": round(ms_layer_serial / ms_layer, 4),
         "wall_s_timed_region": t_wall,
         "loop_clock_ghz": None if loop_ghz is None else round(loop_ghz, 3),
         "pct_of_peak_at_loop_clock": None if loop_ghz is None else

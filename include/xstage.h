@@ -112,6 +112,32 @@ int xstage_ulysses_attn_fwd(const void* const* q_src, const void* const* k_src,
                             const void* const* v_src, void* const* out_dst, int B, int S, int H,
                             int H_local, int h0, int D, int P, float scale, void* stream);
 
+/* The pre-attention all-to-all of a Ulysses layer as a separate step (serial layer): copies
+ * heads [h0, h0 + H_local) of the P sequence shards src_shards[p] ([B, S/P, H, D], HOST
+ * array of device pointers) into the contiguous out [B, S, H_local, D]:
+ *   out[b][s][h][d] = src_shards[s / (S/P)][b][s % (S/P)][h0 + h][d].
+ * Requires 0 < H_local <= H, 0 <= h0 <= H - H_local (else XSTAGE_ERR_INVALID); out must not
+ * overlap any shard. */
+int xstage_ulysses_gather(const void* const* src_shards, void* out, int B, int S, int H, int H_local,
+                          int h0, int D, int P, void* stream);
+
+/* The post-attention all-to-all into full-head receive buffers as a separate step: copies
+ * the contiguous in [B, S, H_local, D] into head columns [h_dst0, h_dst0 + H_local) of
+ * out_dst[p] ([B, S/P, H_dst, D]); every other element is left untouched.  Requirements as
+ * for xstage_attn_a2a_fwd_strided (in in place of q, k, v). */
+int xstage_a2a_scatter_strided(const void* in, void* const* out_dst, int B, int S, int H_local,
+                               int D, int P, int H_dst, int h_dst0, void* stream);
+
+/* Serial version of xstage_ulysses_attn_fwd: xstage_ulysses_gather of q, k and v into the
+ * workspace, xstage_attn_fwd there, then xstage_a2a_scatter_strided into out_dst, all on
+ * `stream`.  workspace: caller-owned, 4 * B * S * H_local * D * 2 bytes (gathered q, k, v
+ * and the attention output), disjoint from every shard and output.  Same result as
+ * xstage_ulysses_attn_fwd, bit for bit. */
+int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_src,
+                                const void* const* v_src, void* workspace, void* const* out_dst,
+                                int B, int S, int H, int H_local, int h0, int D, int P, float scale,
+                                void* stream);
+
 /* The separate all-to-all send step of the serial baseline: copies a contiguous
  * [B, S, H_local, D] tensor into the P slabs.  Slabs must not overlap `in` or each other. */
 int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int H_local,

@@ -47,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -399,3 +399,37 @@ def test_moe_rejects(L):
     offs = (_lib.ctypes.c_int * 6)(*MOE_OFFS)
     assert L.xstage_moe_waves_plan(5, offs, 256, 128, 2, 0, None, arr, _lib.ctypes.byref(n), _lib.ctypes.byref(n)) == INVALID
     assert L.xstage_moe_waves_plan(5, offs, 256, 100, 2, 0, arr, arr, _lib.ctypes.byref(n), _lib.ctypes.byref(n)) == INVALID
+
+
+@no_device
+def test_serial_ulysses_rejects(L):
+    P = 4
+    qs = [0x10_0000_0000 + p * GAP for p in range(P)]
+    ks = [0x20_0000_0000 + p * GAP for p in range(P)]
+    vs = [0x30_0000_0000 + p * GAP for p in range(P)]
+    ds = slabs(P)
+    WS = 0x80_0000_0000
+    arr = lambda x: _lib.ptr_array(x)[0]
+    g = L.xstage_ulysses_gather
+    assert g(arr(qs), WS, 1, 256, 8, 0, 2, 64, P, None) == INVALID          # H_local = 0
+    assert g(arr(qs), WS, 1, 256, 8, 2, 7, 64, P, None) == INVALID          # heads past H
+    assert g(arr(qs), 0, 1, 256, 8, 2, 2, 64, P, None) == INVALID           # no output
+    assert g(arr(qs), qs[1] + 64, 1, 256, 8, 2, 2, 64, P, None) == INVALID  # output inside a shard
+    assert g(arr([qs[0], 0, qs[2], qs[3]]), WS, 1, 256, 8, 2, 2, 64, P, None) == INVALID
+    assert g(arr(qs), WS, 1, 258, 8, 2, 2, 64, P, None) == INVALID          # S % P
+    sc = L.xstage_a2a_scatter_strided
+    assert sc(WS, arr(ds), 1, 256, 2, 64, P, 1, 0, None) == INVALID         # H_dst < H_local
+    assert sc(WS, arr(ds), 1, 256, 2, 64, P, 8, 7, None) == INVALID         # columns past H_dst
+    assert sc(0, arr(ds), 1, 256, 2, 64, P, 8, 2, None) == INVALID
+    assert sc(ds[0] + 64, arr(ds), 1, 256, 2, 64, P, 8, 2, None) == INVALID  # input inside an output
+    u = L.xstage_ulysses_attn_unfused
+    args = lambda **kw: dict(q=arr(qs), k=arr(ks), v=arr(vs), ws=WS, d=arr(ds), B=1, S=256, H=8, Hl=2, h0=2,
+                             D=64, P=P, scale=0.125) | kw
+    call = lambda a: u(a["q"], a["k"], a["v"], a["ws"], a["d"], a["B"], a["S"], a["H"], a["Hl"], a["h0"], a["D"],
+                       a["P"], a["scale"], None)
+    assert call(args(ws=0)) == INVALID
+    assert call(args(ws=ks[2] + 16)) == INVALID                  # workspace inside a shard
+    assert call(args(d=arr([ds[0], ds[1], WS + 64, ds[3]]))) == INVALID  # output inside the workspace
+    assert call(args(scale=float("nan"))) == INVALID
+    assert call(args(h0=7)) == INVALID
+    assert call(args(D=96)) == UNSUPPORTED

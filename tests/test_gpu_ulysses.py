@@ -157,3 +157,52 @@ def test_bound_ulysses_equals_direct():
     f()
     torch.cuda.synchronize()
     assert np.array_equal(a.slabs_host(), b.slabs_host())
+
+
+COPY_SHAPES = [
+    # (B, S, H, H_local, h0, D, P)
+    (2, 1000, 4, 2, 2, 128, 8),   # 125-row shards
+    (1, 64, 2, 1, 1, 64, 8),      # 8-row shards
+    (1, 4608, 24, 3, 15, 128, 8), # FLUX-1024 group, rank 5
+]
+
+
+@pytest.mark.parametrize("B,S,H,Hl,h0,D,P", COPY_SHAPES)
+def test_separate_all_to_alls_bit_exact(B, S, H, Hl, h0, D, P):
+    """The serial layer's copies: the gather equals slicing the rank's heads out of the full
+    tensor, the strided scatter equals the oracle's full-head scatter, bit for bit."""
+    log(f"separate all-to-alls: B={B} S={S} H={H} H_local={Hl} h0={h0} D={D} P={P}")
+    rng = np.random.default_rng(S + H)
+    full = rng.integers(0, 0x7F00, size=(B, S, H, D), dtype=np.uint16)
+    shards = [to_dev(x) for x in shards_of(full, P)]
+    out = torch.full((B, S, Hl, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xs.xstage_ulysses_gather(shards, out, Hl, h0)
+    torch.cuda.synchronize()
+    from tests.gpu_util import to_host
+    assert np.array_equal(to_host(out), full[:, :, h0:h0 + Hl])
+    local = rng.integers(0, 0x7F00, size=(B, S, Hl, D), dtype=np.uint16)
+    dst = GuardedSlabs(P, B, S // P, H, D)
+    xs.xstage_a2a_scatter_strided(to_dev(local), dst.views, h0)
+    torch.cuda.synchronize()
+    assert dst.guards_intact()
+    expect = [np.full((B, S // P, H, D), NAN_BF16, dtype=np.uint16) for _ in range(P)]
+    oracle.scatter_heads(local, expect, h0)
+    assert np.array_equal(dst.slabs_host(), np.stack(expect))
+
+
+@pytest.mark.parametrize("B,S,H,Hl,h0,D,P", COPY_SHAPES)
+def test_ulysses_unfused_equals_fused(B, S, H, Hl, h0, D, P):
+    log(f"ulysses unfused == fused: B={B} S={S} H={H} H_local={Hl} h0={h0} D={D} P={P}")
+    w = Workload("ulysses-serial", B, S, H, D, P, seed=61 + S + H)
+    qb, kb, vb = make_inputs(w)
+    qs, ks, vs = ([to_dev(x) for x in shards_of(t, P)] for t in (qb, kb, vb))
+    fused = GuardedSlabs(P, B, S // P, H, D)
+    xs.xstage_ulysses_attn_fwd(qs, ks, vs, fused.views, Hl, h0, w.scale)
+    serial = GuardedSlabs(P, B, S // P, H, D)
+    ws = torch.empty((4, B, S, Hl, D), dtype=torch.bfloat16, device="cuda")
+    xs.xstage_ulysses_attn_unfused(qs, ks, vs, ws, serial.views, Hl, h0, w.scale)
+    torch.cuda.synchronize()
+    assert serial.guards_intact()
+    got = serial.slabs_host()
+    assert np.array_equal(got, fused.slabs_host())
+    assert np.all(got[:, :, :, :h0] == NAN_BF16) and np.all(got[:, :, :, h0 + Hl:] == NAN_BF16)
