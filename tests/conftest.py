@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not failed) when no device is visible; on a GPU machine a missing
+    # GPU tests are skipped (not failed) when no device is visible; with a device, a missing
     # library is an error raised by the binding, never a silent fallback.
     try:
         import torch
