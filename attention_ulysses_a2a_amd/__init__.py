@@ -40,6 +40,7 @@ __all__ = [
     "xstage_ulysses_gather",
     "xstage_a2a_scatter_strided",
     "xstage_ulysses_attn_unfused",
+    "xstage_ulysses_attn_fwd_kv_staged",
     "xstage_attn_a2a_plan",
     "xstage_attn_a2a_schedule",
     "xstage_attn_a2a_fwd_traced",
@@ -192,6 +193,19 @@ def xstage_ulysses_attn_unfused(q_src, k_src, v_src, workspace, out_dst, H_local
         st = lib().xstage_ulysses_attn_unfused(*call)
     del keep
     _check(st, "xstage_ulysses_attn_unfused")
+
+
+def xstage_ulysses_attn_fwd_kv_staged(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=None,
+                                      stream=None) -> None:
+    """Ulysses layer with K and V gathered into ``workspace`` (2 x [B, S, H_local, D] bf16)
+    and Q read from the shards in place; same output as xstage_ulysses_attn_fwd."""
+    import torch
+
+    call, keep, dev = _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream)
+    with torch.cuda.device(dev):
+        st = lib().xstage_ulysses_attn_fwd_kv_staged(*call)
+    del keep
+    _check(st, "xstage_ulysses_attn_fwd_kv_staged")
 
 
 def xstage_attn_a2a_fwd_strided(q, k, v, out_dst, h_dst0, scale=None, stream=None) -> None:
@@ -442,7 +456,8 @@ def bind(name: str, *args, **kwargs) -> _Bound:
     made with that device current.  Supported: xstage_attn_a2a_fwd, xstage_attn_fwd,
     xstage_a2a_scatter, xstage_attn_a2a_unfused, xstage_attn_a2a_fwd_traced,
     xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd, xstage_ulysses_attn_unfused,
-    xstage_moe_waves_run, with the same arguments as the functions.
+    xstage_ulysses_attn_fwd_kv_staged, xstage_moe_waves_run, with the same arguments as the
+    functions.
     """
     import torch
 
@@ -501,7 +516,7 @@ def bind(name: str, *args, **kwargs) -> _Bound:
         scale, stream = kwargs.get("scale", args[6] if len(args) > 6 else None), kwargs.get("stream")
         call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
         refs = (q_src, k_src, v_src, out_dst, keep)
-    elif name == "xstage_ulysses_attn_unfused":
+    elif name in ("xstage_ulysses_attn_unfused", "xstage_ulysses_attn_fwd_kv_staged"):
         q_src, k_src, v_src, workspace, out_dst, H_local, h0 = args[:7]
         scale, stream = kwargs.get("scale", args[7] if len(args) > 7 else None), kwargs.get("stream")
         call, keep, dev = _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream)

@@ -80,6 +80,8 @@ SIGNATURES = {
     "xstage_ulysses_gather": (_i, [_PP, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "xstage_a2a_scatter_strided": (_i, [_vp, _PP, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "xstage_ulysses_attn_unfused": (_i, [_PP, _PP, _PP, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp]),
+    "xstage_ulysses_attn_fwd_kv_staged": (
+        _i, [_PP, _PP, _PP, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp]),
     "xstage_attn_a2a_plan": (_i, [_i, _i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "xstage_attn_a2a_schedule": (_i, [_i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 5),
     "xstage_attn_a2a_fwd_traced": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp, _vp]),

@@ -229,6 +229,48 @@ int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_s
   return launch_slice_copy(osrc, 0, H_local * D, 0, out_dst, 1, H * D, h0 * D, B, S, H_local, D, P, s);
 }
 
+int xstage_ulysses_attn_fwd_kv_staged(const void* const* q_src, const void* const* k_src, const void* const* v_src,
+                                      void* workspace, void* const* out_dst, int B, int S, int H, int H_local, int h0,
+                                      int D, int P, float scale, void* stream) {
+  int st = check_shape(B, S, H, D, P);
+  if (st != XSTAGE_OK) return st;
+  if (H_local <= 0 || H_local > H || h0 < 0 || h0 > H - H_local) return XSTAGE_ERR_INVALID;
+  if (P > kMaxSrc) return XSTAGE_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace) || !std::isfinite(scale)) return XSTAGE_ERR_INVALID;
+  const unsigned long long shard = tensor_bytes(B, S, H, D) / (unsigned long long)P;
+  const unsigned long long tl = tensor_bytes(B, S, H_local, D);
+  std::vector<Range> src;
+  for (const void* const* t : {q_src, k_src, v_src}) {
+    st = collect_shards(t, P, shard, &src);
+    if (st != XSTAGE_OK) return st;
+  }
+  const Range ws = range_of(workspace, 2 * tl);
+  if (!disjoint_from(ws, src)) return XSTAGE_ERR_INVALID;
+  std::vector<Range> others = src;
+  others.push_back(ws);
+  st = check_slabs(out_dst, P, shard, others.data(), (int)others.size());
+  if (st != XSTAGE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  void* kc[1] = {w};
+  void* vc[1] = {w + tl};
+  st = launch_slice_copy(k_src, 1, H * D, h0 * D, kc, 0, H_local * D, 0, B, S, H_local, D, P, s);
+  if (st != XSTAGE_OK) return st;
+  st = launch_slice_copy(v_src, 1, H * D, h0 * D, vc, 0, H_local * D, 0, B, S, H_local, D, P, s);
+  if (st != XSTAGE_OK) return st;
+  SrcTable t = {};
+  for (int p = 0; p < P; ++p) t.q[p] = static_cast<const uint16_t*>(q_src[p]);
+  Layout lay;
+  lay.src = &t;
+  lay.kv_contiguous = 1;
+  lay.src_heads = H;
+  lay.src_head0 = h0;
+  lay.dst_heads = H;
+  lay.dst_head0 = h0;
+  return launch_attn_any(q_src[0], kc[0], vc[0], make_table(out_dst, P), B, S, H_local, D, P, scale, s, 0, nullptr,
+                         &lay);
+}
+
 int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_split) {
   if (n_workgroups == nullptr) return XSTAGE_ERR_INVALID;
   const int st = check_shape(B, S, H_local, D, 1);

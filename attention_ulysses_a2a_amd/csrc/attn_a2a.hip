@@ -107,9 +107,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 
 struct NoSrc {};
 
-template <int D, int MODE, bool SRC>
+// Where q, k, v come from: kPlain = contiguous [B, S, H, D] tensors (a.q, a.k, a.v);
+// kShards = Q, K and V read in place from P sequence shards (the SrcTable); kShardQ = Q from
+// the shards, K and V from contiguous [B, S, H, D] tensors (a.k, a.v).
+enum SrcMode { kPlain = 0, kShards = 1, kShardQ = 2 };
+
+template <int D, int MODE, int SRC>
 __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, const UnitTable tab,
-                                                          const std::conditional_t<SRC, SrcTable, NoSrc> src) {
+                                                          const std::conditional_t<SRC != kPlain, SrcTable, NoSrc> src) {
   // The body names device-only types (the buffer resource), which the host pass of a
   // template cannot instantiate; the host pass only needs the launch signature.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -178,9 +183,13 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   const int b = bh / a.H;
   const int m0 = mt * C::BM;
   const int S = a.S;
-  const uint32_t rs = (uint32_t)a.src_hs * D;  // elements between consecutive rows of one head
-  // offset of (b, first row of a shard, this head) within a shard
-  const uint32_t head0 = ((uint32_t)b * a.src_rows * a.src_hs + a.src_h0 + h) * D;
+  // Q rows: rq elements apart; qhead0 = offset of (b, first row of a shard, this head) within
+  // a shard (the whole tensor when it is not sharded).  K/V rows: the same unless kShardQ.
+  const uint32_t rq = (uint32_t)a.src_hs * D;
+  const uint32_t qhead0 = ((uint32_t)b * a.src_rows * a.src_hs + a.src_h0 + h) * D;
+  const uint32_t rs = SRC == kShardQ ? (uint32_t)a.H * D : rq;  // elements between K/V rows
+  const uint32_t head0 = SRC == kShardQ ? ((uint32_t)b * S * a.H + h) * D : qhead0;
+  const int kv_rows = SRC == kShardQ ? S : a.src_rows;  // rows per K/V buffer
 
   // Q fragment (B operand of the score MFMA): lane holds query (lane & 31), d = 16ks + 8*hl + 0..7
   bf16x8 qf[C::KS];
@@ -192,14 +201,14 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       if (qrow < S) {
         const uint16_t* qb;
         int r = qrow;
-        if constexpr (SRC) {
+        if constexpr (SRC != kPlain) {
           const int p = qrow / a.src_rows;
           r = qrow - p * a.src_rows;
-          qb = src.q[p] + head0;
+          qb = src.q[p] + qhead0;
         } else {
-          qb = a.q + head0;
+          qb = a.q + qhead0;
         }
-        x = *reinterpret_cast<const u32x4*>(qb + (uint32_t)r * rs + ks * 16 + hl * 8);
+        x = *reinterpret_cast<const u32x4*>(qb + (uint32_t)r * rq + ks * 16 + hl * 8);
       }
       x ^= a.qflip;
       qf[ks] = __builtin_bit_cast(bf16x8, x);
@@ -214,19 +223,19 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   // offset (the scalar offset stays 0, so the range check sees the whole offset): rows
   // past the end of the sequence read as zeros — no clamping, no branches.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int head_bytes = (int)((uint32_t)a.src_rows * rs * 2u);  // one shard's rows of this head
+  const int head_bytes = (int)((uint32_t)kv_rows * rs * 2u);  // one K/V buffer's rows of this head
   auto make_rsrc = [&](const uint16_t* base) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + head0), (short)0, head_bytes, 0x00020000);
   };
-  // One shard (SRC = false): the buffer resources are fixed.  Shards (SRC = true): they are
-  // built per block from the shard pointer (kernel arguments, scalar loads); the tables
-  // index 0 = K, 1 = V.
+  // K/V in one buffer (kPlain, kShardQ): the buffer resources are fixed.  K/V in shards
+  // (kShards): they are built per block from the shard pointer (kernel arguments, scalar
+  // loads).
   __amdgpu_buffer_rsrc_t krsrc, vrsrc;
-  // Shard cursors (SRC): first row of the shard holding the K (V) stream's current block and
+  // Shard cursors (kShards): first row of the shard holding the K (V) stream's current block and
   // that shard's resource; blocks only move forward, from j0.
   int k_lo = 0, v_lo = 0;
   __amdgpu_buffer_rsrc_t k_r, v_r;
-  if constexpr (!SRC) {
+  if constexpr (SRC != kShards) {
     krsrc = make_rsrc(a.k);
     vrsrc = make_rsrc(a.v);
   } else {
@@ -243,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
     ld_voff[i] = ((uint32_t)row * rs + (uint32_t)((pc ^ swz<D>(row)) * 8)) * 2u;
   }
   auto dload = [&](const __amdgpu_buffer_rsrc_t& rsrc, int slot_byte, int n0) {
-    if constexpr (!SRC) {
+    if constexpr (SRC != kShards) {
       const uint32_t boff = (uint32_t)n0 * rs * 2u;
 #pragma unroll
       for (int i = 0; i < C::NLD; ++i)
@@ -714,13 +723,16 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   const NoSrc none;
   if (lay.src) {  // shards: product mode only
     if (mode != kRun) return XSTAGE_ERR_INVALID;
-    hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, true>), grid, block, 0, stream, a, t, *lay.src);
+    if (lay.kv_contiguous)
+      hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kShardQ>), grid, block, 0, stream, a, t, *lay.src);
+    else
+      hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kShards>), grid, block, 0, stream, a, t, *lay.src);
   } else {
     switch (mode) {
-      case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced, false>), grid, block, 0, stream, a, t, none); break;
-      case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled, false>), grid, block, 0, stream, a, t, none); break;
-      case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore, false>), grid, block, 0, stream, a, t, none); break;
-      default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, false>), grid, block, 0, stream, a, t, none); break;
+      case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced, kPlain>), grid, block, 0, stream, a, t, none); break;
+      case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled, kPlain>), grid, block, 0, stream, a, t, none); break;
+      case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore, kPlain>), grid, block, 0, stream, a, t, none); break;
+      default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kPlain>), grid, block, 0, stream, a, t, none); break;
     }
   }
   return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
@@ -765,8 +777,8 @@ int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, in
 
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
                     int P, float scale, hipStream_t stream, int mode, unsigned long long* stamps, const Layout* layout) {
-  static const Layout kPlain;
-  const Layout& lay = layout ? *layout : kPlain;
+  static const Layout kDefaultLayout;
+  const Layout& lay = layout ? *layout : kDefaultLayout;
   const int n_tiles = B * H * ((S + 127) / 128);
   const int nkv = (S + 63) / 64;
   SplitPlan plan = choose_split(n_tiles, nkv, D, partial_bytes_per_unit(D));

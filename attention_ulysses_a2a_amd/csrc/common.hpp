@@ -41,6 +41,8 @@ struct Layout {
   const SrcTable* src = nullptr;  // non-null: inputs are P shards [B, S/P, src_heads, D]
   int src_heads = 0, src_head0 = 0;  // shard row width (heads) and this call's first head
   int dst_heads = 0, dst_head0 = 0;  // slab row width (heads) and this call's first column
+  int kv_contiguous = 0;  // with src: only Q from the shards, K and V from contiguous
+                          // [B, S, H_local, D] tensors (the k, v arguments)
 };
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -184,7 +184,10 @@ def bench_attention(args, torch, xs):
                            w.scale)
     ms_strided = timed(strided, args.steps, leg_warmup, torch)
     ms_layer = timed(layer, args.steps, leg_warmup, torch)
+    layer_staged = xs.bind("xstage_ulysses_attn_fwd_kv_staged", shards[0], shards[1], shards[2], ws4[:2], recv,
+                           w.H, h0, w.scale)
     ms_layer_serial = timed(layer_serial, args.steps, leg_warmup, torch)
+    ms_layer_staged = timed(layer_staged, args.steps, leg_warmup, torch)
     del shards, recv, ws4
 
     # Core clock during the key loop (traced call, mode 3: shader-clock ticks against
@@ -238,6 +241,8 @@ def bench_attention(args, torch, xs):
         "ulysses_layer_TFLOPs": round(w.flops / (ms_layer * 1e-3) / 1e12, 3),
         "ms_ulysses_layer_serial": ms_layer_serial,
         "ulysses_fused_vs_serial": round(ms_layer_serial / ms_layer, 4),
+        "ms_ulysses_layer_kv_staged": ms_layer_staged,
+        "ulysses_kv_staged_vs_in_place": round(ms_layer / ms_layer_staged, 4),
         "wall_s_timed_region": t_wall,
         "loop_clock_ghz": None if loop_ghz is None else round(loop_ghz, 3),
         "pct_of_peak_at_loop_clock": None if loop_ghz is None else

@@ -138,6 +138,22 @@ int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_s
                                 int B, int S, int H, int H_local, int h0, int D, int P, float scale,
                                 void* stream);
 
+/* Ulysses layer with K and V staged: xstage_ulysses_gather of k and v into the workspace,
+ * then one attention launch that reads Q from the shards in place and writes its output
+ * into out_dst as xstage_ulysses_attn_fwd does, all on `stream`.  Every query tile reads
+ * all of K and V, so at long sequences the gathered copies keep those reads to one
+ * contiguous buffer each, while Q (read once) and the output (written once) keep the
+ * fused all-to-all.  Measured on MI355X (H_local = H/8, D = 128): 6 to 9 % faster than
+ * xstage_ulysses_attn_fwd once one tensor's shards span about 100 MB or more
+ * (S * H * D * 2 bytes), slower at 28 MB, where the two extra launches cost more than the
+ * in-place reads lose.  workspace: caller-owned, 2 * B * S * H_local * D * 2 bytes (k,
+ * then v), disjoint from every shard and output.  Requirements and result as for
+ * xstage_ulysses_attn_fwd, bit for bit. */
+int xstage_ulysses_attn_fwd_kv_staged(const void* const* q_src, const void* const* k_src,
+                                      const void* const* v_src, void* workspace,
+                                      void* const* out_dst, int B, int S, int H, int H_local,
+                                      int h0, int D, int P, float scale, void* stream);
+
 /* The separate all-to-all send step of the serial baseline: copies a contiguous
  * [B, S, H_local, D] tensor into the P slabs.  Slabs must not overlap `in` or each other. */
 int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int H_local,

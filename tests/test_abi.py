@@ -47,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -433,3 +433,18 @@ def test_serial_ulysses_rejects(L):
     assert call(args(scale=float("nan"))) == INVALID
     assert call(args(h0=7)) == INVALID
     assert call(args(D=96)) == UNSUPPORTED
+    # K/V-staged layer: same argument list, workspace of 2 x [B, S, H_local, D]
+    kv = L.xstage_ulysses_attn_fwd_kv_staged
+    kcall = lambda a: kv(a["q"], a["k"], a["v"], a["ws"], a["d"], a["B"], a["S"], a["H"], a["Hl"], a["h0"], a["D"],
+                         a["P"], a["scale"], None)
+    tl = 1 * 256 * 2 * 64 * 2
+    assert kcall(args(ws=0)) == INVALID
+    assert kcall(args(ws=WS + 8)) == INVALID                     # misaligned workspace
+    assert kcall(args(ws=vs[3] + 16)) == INVALID                 # workspace inside a shard
+    assert kcall(args(d=arr([ds[0], WS + tl + 64, ds[2], ds[3]]))) == INVALID  # output inside its second half
+    assert kcall(args(q=arr([qs[0], 0, qs[2], qs[3]]))) == INVALID
+    assert kcall(args(scale=float("inf"))) == INVALID
+    assert kcall(args(Hl=0)) == INVALID
+    assert kcall(args(D=96)) == UNSUPPORTED
+    big = [SLAB0 + p * GAP for p in range(33)]
+    assert kcall(args(q=arr(big), k=arr(big), v=arr(big), d=arr(big), S=33 * 8, P=33)) == UNSUPPORTED

@@ -9,6 +9,8 @@
   (oracle.ulysses_attention: explicit gather, fp64 attention, explicit scatter), full at
   small shapes and on sampled query rows at the FLUX-1024 and video groups; shard sizes
   that are odd or below one 64-key block make key blocks straddle shards;
+* xstage_ulysses_attn_fwd_kv_staged (K and V gathered into a workspace, Q read in place)
+  equals xstage_ulysses_attn_fwd bit for bit at every layer shape;
 * the placement probe (exact output = V) through both all-to-alls, bit-exact.
 """
 
@@ -114,11 +116,16 @@ def test_ulysses_layer(B, S, H, Hl, h0, D, P, full):
     ref = GuardedSlabs(P, B, S // P, H, D)
     qc, kc, vc = (to_dev(np.ascontiguousarray(t[:, :, h0:h0 + Hl])) for t in (qb, kb, vb))
     xs.xstage_attn_a2a_fwd_strided(qc, kc, vc, ref.views, h0, w.scale)
+    # K and V staged in a workspace, Q read from the shards
+    staged = GuardedSlabs(P, B, S // P, H, D)
+    ws = torch.full((2, B, S, Hl, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xs.xstage_ulysses_attn_fwd_kv_staged(qs, ks, vs, ws, staged.views, Hl, h0, w.scale)
     torch.cuda.synchronize()
-    assert out.guards_intact()
+    assert out.guards_intact() and staged.guards_intact()
     got = out.slabs_host()
     assert np.all(got[:, :, :, :h0] == NAN_BF16) and np.all(got[:, :, :, h0 + Hl:] == NAN_BF16)
     assert np.array_equal(got, ref.slabs_host())
+    assert np.array_equal(staged.slabs_host(), got)
     # values against the oracle's layer (explicit gather, fp64 attention, explicit scatter)
     rows = None if full else sample_rows(S, P)
     f64 = [[oracle.bf16_bits_to_f64(x) for x in shards_of(t, P)] for t in (qb, kb, vb)]
@@ -137,11 +144,15 @@ def test_ulysses_placement_probe(B, S, H, Hl, h0, D, P):
     qs, ks, vs = ([to_dev(x) for x in shards_of(t, P)] for t in (pq, pk, pv))
     out = GuardedSlabs(P, B, S // P, H, D)
     xs.xstage_ulysses_attn_fwd(qs, ks, vs, out.views, Hl, h0, scale)
+    staged = GuardedSlabs(P, B, S // P, H, D)
+    ws = torch.empty((2, B, S, Hl, D), dtype=torch.bfloat16, device="cuda")
+    xs.xstage_ulysses_attn_fwd_kv_staged(qs, ks, vs, ws, staged.views, Hl, h0, scale)
     torch.cuda.synchronize()
-    assert out.guards_intact()
+    assert out.guards_intact() and staged.guards_intact()
     got = out.slabs_host()
     assert np.array_equal(got[:, :, :, h0:h0 + Hl], oracle.ulysses_scatter(pv, P)[:, :, :, h0:h0 + Hl])
     assert np.all(got[:, :, :, :h0] == NAN_BF16) and np.all(got[:, :, :, h0 + Hl:] == NAN_BF16)
+    assert np.array_equal(staged.slabs_host(), got)
 
 
 def test_bound_ulysses_equals_direct():
