@@ -12,5 +12,6 @@ from .inputs import (  # noqa: F401
     f32_to_bf16_bits,
     make_inputs,
     make_placement_probe,
+    make_placement_probe_torch,
     workload,
 )

@@ -153,3 +153,33 @@ def make_placement_probe(B: int, S: int, H: int, D: int, scale: float, seed: int
     v[..., 3] = np.arange(B)[:, None, None]
     qb = f32_to_bf16_bits(qk)
     return qb, qb.copy(), f32_to_bf16_bits(v)
+
+
+def make_placement_probe_torch(B: int, S: int, H: int, D: int, scale: float, device, seed: int = 7,
+                               margin: float = 120.0):
+    """make_placement_probe's (q, k, v), bit for bit, assembled with torch on ``device`` and
+    returned as bf16 tensors: the same codes and sign vectors (drawn on the host), the same
+    broadcast products and tags, cast fp32 -> bf16 with round-to-nearest-even.  For tensors
+    of billions of elements, whose host-side assembly would take minutes."""
+    import torch
+
+    if D < 4:
+        raise ValueError("placement probe needs D >= 4 for its tags")
+    codes = _probe_codes(S, D, float(scale), seed, float(margin))
+    rng = np.random.default_rng(seed + 1)
+    sigma = (rng.integers(0, 2, size=(B, H, D), dtype=np.int8) * 2 - 1).astype(np.float32)
+    c = torch.from_numpy(codes.astype(np.float32)).to(device)
+    sg = torch.from_numpy(sigma).to(device)
+    q = (8.0 * c[None, :, None, :] * sg[:, None, :, :]).to(torch.bfloat16)
+    i32 = dict(device=device, dtype=torch.int32)
+    s_idx = torch.arange(S, **i32)[None, :, None, None]
+    h_idx = torch.arange(H, **i32)[None, None, :, None]
+    b_idx = torch.arange(B, **i32)[:, None, None, None]
+    d_idx = torch.arange(D, **i32)[None, None, None, :]
+    v = ((s_idx * 7 + d_idx * 13 + h_idx * 31 + b_idx * 17) % 256 - 128).to(torch.float32)
+    v[..., 0] = (torch.arange(S, **i32) % 256).to(torch.float32)[None, :, None]
+    v[..., 1] = (torch.arange(S, **i32) // 256).to(torch.float32)[None, :, None]
+    v[..., 2] = torch.arange(H, **i32).to(torch.float32)[None, None, :]
+    v[..., 3] = torch.arange(B, **i32).to(torch.float32)[:, None, None]
+    v = v.to(torch.bfloat16)
+    return q, q.clone(), v

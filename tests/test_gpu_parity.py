@@ -18,7 +18,7 @@ import torch
 
 import attention_ulysses_a2a_amd as xs
 import oracle
-from synth import Workload, make_inputs, make_placement_probe, workload
+from synth import Workload, make_inputs, make_placement_probe, make_placement_probe_torch, workload
 from tests.gpu_util import NAN_BF16, GuardedSlabs, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -181,6 +181,26 @@ def test_placement_sized_key_ranges(B, S, H, D, P, full):
     gp = run_fused(w, pq, pk, pv, w.scale)
     assert gp.guards_intact()
     assert np.array_equal(gp.slabs_host(), oracle.ulysses_scatter(pv, P))
+
+
+def test_largest_supported_tensor():
+    """One tensor of B*S*H*D elements just below 2^31, the largest the entry points accept
+    (element offsets are 32-bit): the placement probe through the fused call, every slab
+    element bit-exact (O = V exactly), guards intact.  S = 32760 gives odd 4095-row slabs
+    and a key tail of 56; the probe is assembled on the device (same bytes as the host
+    generator, checked on the CPU)."""
+    B, S, H, D, P = 1, 32760, 512, 128, 8
+    assert B * S * H * D < 2 ** 31 <= B * S * (H + 1) * D
+    scale = 1.0 / np.sqrt(D)
+    log(f"largest tensor: B={B} S={S} H={H} D={D} P={P} ({B * S * H * D} elements)")
+    q, k, v = make_placement_probe_torch(B, S, H, D, scale, "cuda")
+    g = GuardedSlabs(P, B, S // P, H, D)
+    xs.xstage_attn_a2a_fwd(q, k, v, g.views, scale)
+    torch.cuda.synchronize()
+    v_host = v.view(torch.int16).cpu().numpy().view(np.uint16)
+    del q, k, v
+    assert g.guards_intact()
+    assert np.array_equal(g.slabs_host(), oracle.ulysses_scatter(v_host, P))
 
 
 def test_attn_fwd_contiguous_matches_oracle():

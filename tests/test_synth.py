@@ -1,10 +1,11 @@
 """The seeded input generator: determinism, bf16 cast, workload structure, probe guarantee."""
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
-from synth import WORKLOADS, f32_to_bf16_bits, make_inputs, make_placement_probe, workload
+from synth import WORKLOADS, f32_to_bf16_bits, make_inputs, make_placement_probe, make_placement_probe_torch, workload
 
 
 def test_bf16_cast_matches_torch_rne():
@@ -69,3 +70,14 @@ def test_placement_probe_output_is_v_exactly():
         assert np.array_equal(oracle.bf16_bits_to_f64(oracle.round_to_bf16_bits(o)), v)  # -0 == +0
         assert np.array_equal(v[0, :, 0, 0], np.arange(S) % 256)
         assert np.array_equal(v[0, :, :, 2][0], np.arange(H))
+
+
+@pytest.mark.parametrize("B,S,H,D", [(1, 64, 2, 128), (2, 130, 3, 64), (1, 40, 300, 64)])
+def test_torch_probe_equals_numpy_probe(B, S, H, D):
+    """The torch assembly of the placement probe (used at the largest tensor size) is the
+    same bytes as the numpy one; H = 300 also covers head tags that round in bf16."""
+    scale = 1.0 / np.sqrt(D)
+    ref = make_placement_probe(B, S, H, D, scale)
+    got = make_placement_probe_torch(B, S, H, D, scale, "cpu")
+    for r, g in zip(ref, got):
+        assert np.array_equal(r, g.view(torch.int16).numpy().view(np.uint16))
