@@ -135,22 +135,24 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int hl = lane >> 5;  // half of the wave
-  unsigned long long t_start = 0, t_loop = 0, c_start = 0, c_loop = 0;
-  if constexpr (MODE != kRun) {
-    t_start = __builtin_amdgcn_s_memrealtime();
-    c_start = __builtin_amdgcn_s_memtime();
-  }
-  auto trace_out = [&](unsigned long long t_issued, unsigned long long t_done) {
+  // Traced modes: each stamp is stored (by lane 0) as soon as it is taken, so that no
+  // stamp stays live across the key loop and the merge.
+  auto stamp = [&](int slot, unsigned long long v) {
     if constexpr (MODE != kRun) {
-      if (lane == 0) {
-        unsigned long long* st = a.stamps + ((size_t)blockIdx.x * 4 + w) * 4;
-        st[0] = t_start;
-        st[1] = t_loop;
-        st[2] = a.clock_stamps ? c_start : t_issued;
-        st[3] = a.clock_stamps ? c_loop : t_done;
-      }
+      if (lane == 0) a.stamps[((size_t)blockIdx.x * 4 + w) * 4 + slot] = v;
     }
   };
+  // Entries 2 and 3 start at 0: a workgroup that stores no output (a split that does not
+  // merge, rows past S, the no-store mode) leaves them so.
+  if constexpr (MODE != kRun) {
+    stamp(0, __builtin_amdgcn_s_memrealtime());
+    if (a.clock_stamps) {
+      stamp(2, __builtin_amdgcn_s_memtime());
+    } else {
+      stamp(2, 0);
+      stamp(3, 0);
+    }
+  }
 
   const int nkv = (a.S + C::BN - 1) / C::BN;
   // This workgroup's tile, split and key-block range [j0, j1).  One-round launches take
@@ -496,8 +498,8 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   }
 
   if constexpr (MODE != kRun) {
-    t_loop = __builtin_amdgcn_s_memrealtime();
-    c_loop = __builtin_amdgcn_s_memtime();
+    stamp(1, __builtin_amdgcn_s_memrealtime());
+    if (a.clock_stamps) stamp(3, __builtin_amdgcn_s_memtime());
   }
 
   // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
@@ -542,10 +544,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       last_flag = is_last;
     }
     __syncthreads();
-    if (!last_flag) {
-      trace_out(0, 0);
-      return;
-    }
+    if (!last_flag) return;
     // Merge in split order (own partial included, as the bits of its record), so the result
     // does not depend on which split arrived last.  Uncached reads have a long latency: the
     // records of NB splits are requested together and folded in with a running-max rescale,
@@ -628,10 +627,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   constexpr int NST = 32 * C::CH / 64;  // 16-byte stores per lane
   // wu: this wave's index as a wave-uniform value (defined with the loads above)
   const int row0 = m0 + wu * 32;
-  if (row0 >= S || MODE == kNoStore) {
-    trace_out(0, 0);
-    return;
-  }
+  if (row0 >= S || MODE == kNoStore) return;
   const int rowN = min(row0 + 31, S - 1);
   const int p_lo = row0 / a.S_P, p_hi = rowN / a.S_P;
   const bool full = row0 + 31 < S;
@@ -681,7 +677,10 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       t_done = __builtin_amdgcn_s_memrealtime();
     }
-    trace_out(t_issued, t_done);
+    if (!a.clock_stamps) {
+      stamp(2, t_issued);
+      stamp(3, t_done);
+    }
   }
 #endif
 }
