@@ -246,13 +246,14 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
     k_r = make_rsrc(uniform_ptr(src.k[p]));
     v_r = make_rsrc(uniform_ptr(src.v[p]));
   }
-  uint32_t ld_voff[C::NLD];  // byte offset of this lane's chunk from the block's first key
-#pragma unroll
-  for (int i = 0; i < C::NLD; ++i) {
-    const int P = (i * 4 + w) * 64 + lane;
-    const int row = P / C::CH, pc = P % C::CH;
-    ld_voff[i] = ((uint32_t)row * rs + (uint32_t)((pc ^ swz<D>(row)) * 8)) * 2u;
-  }
+  // Byte offset of this lane's chunk from the block's first key, for its first load; load i
+  // of the lane is RSTEP rows further on (the swizzle repeats every 16 rows, so the chunk
+  // column is the same): one per-lane register, the rest is a wave-uniform offset.
+  constexpr int RSTEP = 4 * 64 / C::CH;
+  static_assert(RSTEP % 16 == 0, "the swizzle must repeat between a lane's loads");
+  const int ld_row = (w * 64 + lane) / C::CH;
+  const uint32_t ld_voff = ((uint32_t)ld_row * rs + (uint32_t)((((w * 64 + lane) % C::CH) ^ swz<D>(ld_row)) * 8)) * 2u;
+  const uint32_t ld_step = (uint32_t)RSTEP * rs * 2u;
   auto dload = [&](const __amdgpu_buffer_rsrc_t& rsrc, int slot_byte, int n0) {
     if constexpr (SRC != kShards) {
       const uint32_t boff = (uint32_t)n0 * rs * 2u;
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       for (int i = 0; i < C::NLD; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
-            ld_voff[i] + boff, 0, 0, 0);
+            ld_voff + (i * ld_step + boff), 0, 0, 0);
     } else {
       // The stream's cursor (K or V: which one is fixed by the slot, a constant after
       // inlining) names the shard holding its current block.  A block inside that shard is
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
         for (int i = 0; i < C::NLD; ++i)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               cur_r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
-              ld_voff[i] + boff, 0, 0, 0);
+              ld_voff + (i * ld_step + boff), 0, 0, 0);
       } else {
         const uint16_t* const* tbl = is_k ? src.k : src.v;
         const int p0 = n0 / a.src_rows, p1 = last / a.src_rows;
@@ -289,11 +290,11 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
           const uint32_t boff = (uint32_t)(n0 - p * a.src_rows) * rs * 2u;
 #pragma unroll
           for (int i = 0; i < C::NLD; ++i) {
-            const int row = ((i * 4 + w) * 64 + lane) / C::CH;
+            const int row = ld_row + i * RSTEP;
             if (row >= lo && row < hi)
               __builtin_amdgcn_raw_ptr_buffer_load_lds(
                   r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
-                  ld_voff[i] + boff, 0, 0, 0);
+                  ld_voff + (i * ld_step + boff), 0, 0, 0);
           }
         }
         cur_lo = p1 * a.src_rows;
