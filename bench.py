@@ -315,7 +315,7 @@ def bench_moe(args, torch, xs):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the P Ulysses destinations are local "
+        print(json.dumps({"error": "bench.py measures one GPU only: the P Ulysses destinations are local "
                                    "receive buffers; no collective or multi-GPU path exists (use --gpus 1)"}))
         sys.exit(2)
     import torch
