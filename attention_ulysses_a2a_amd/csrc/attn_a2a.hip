@@ -225,22 +225,22 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   // offset (the scalar offset stays 0, so the range check sees the whole offset): rows
   // past the end of the sequence read as zeros — no clamping, no branches.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int head_bytes = (int)((uint32_t)kv_rows * rs * 2u);  // one K/V buffer's rows of this head
+  const uint32_t head_bytes = (uint32_t)kv_rows * rs * 2u;  // one K/V buffer's rows of this head
   auto make_rsrc = [&](const uint16_t* base) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + head0), (short)0, head_bytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + head0), (short)0, (int)head_bytes, 0x00020000);
   };
-  // K/V in one buffer (kPlain, kShardQ): the buffer resources are fixed.  K/V in shards
-  // (kShards): they are built per block from the shard pointer (kernel arguments, scalar
-  // loads).
-  __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+  // K/V in one buffer (kPlain, kShardQ): every block gets a resource that starts at its
+  // first row and spans the rows left in the head (wave-uniform scalar arithmetic), so the
+  // per-lane offsets stay fixed through the loop and the range check still zeroes rows past
+  // the end.  K/V in shards (kShards): the resources are built from the shard pointers
+  // (kernel arguments, scalar loads) and the block offset is in the per-lane offset.
+  const uint16_t* const kbase = SRC != kShards ? a.k + head0 : nullptr;
+  const uint16_t* const vbase = SRC != kShards ? a.v + head0 : nullptr;
   // Shard cursors (kShards): first row of the shard holding the K (V) stream's current block and
   // that shard's resource; blocks only move forward, from j0.
   int k_lo = 0, v_lo = 0;
   __amdgpu_buffer_rsrc_t k_r, v_r;
-  if constexpr (SRC != kShards) {
-    krsrc = make_rsrc(a.k);
-    vrsrc = make_rsrc(a.v);
-  } else {
+  if constexpr (SRC == kShards) {
     const int p = j0 * C::BN / a.src_rows;
     k_lo = v_lo = p * a.src_rows;
     k_r = make_rsrc(uniform_ptr(src.k[p]));
@@ -254,14 +254,17 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   const int ld_row = (w * 64 + lane) / C::CH;
   const uint32_t ld_voff = ((uint32_t)ld_row * rs + (uint32_t)((((w * 64 + lane) % C::CH) ^ swz<D>(ld_row)) * 8)) * 2u;
   const uint32_t ld_step = (uint32_t)RSTEP * rs * 2u;
-  auto dload = [&](const __amdgpu_buffer_rsrc_t& rsrc, int slot_byte, int n0) {
+  // base: kbase or vbase (unused with shards: the slot names the stream).
+  auto dload = [&](const uint16_t* base, int slot_byte, int n0) {
     if constexpr (SRC != kShards) {
-      const uint32_t boff = (uint32_t)n0 * rs * 2u;
+      const uint32_t boff = (uint32_t)n0 * rs * 2u;  // < head_bytes: n0 < S
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(base + (size_t)n0 * rs), (short)0, (int)(head_bytes - boff), 0x00020000);
 #pragma unroll
       for (int i = 0; i < C::NLD; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
-            ld_voff + (i * ld_step + boff), 0, 0, 0);
+            ld_voff + i * ld_step, 0, 0, 0);
     } else {
       // The stream's cursor (K or V: which one is fixed by the slot, a constant after
       // inlining) names the shard holding its current block.  A block inside that shard is
@@ -394,7 +397,9 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][r], c, neg_m));
-    float rs4[4];
+    // The row sum accumulates straight into l_run (one chain of 16 dot products: no
+    // zero-initialised partial sums to add up afterwards).
+    float l = l_run;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x16& x = st[q >> 1];
@@ -403,13 +408,13 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       // of the 4-word vector has been miscompiled into four dot products of the first word)
       const uint32_t w0 = pack_bf16x2(x[r0 + 0], x[r0 + 1]), w1 = pack_bf16x2(x[r0 + 2], x[r0 + 3]);
       const uint32_t w2 = pack_bf16x2(x[r0 + 4], x[r0 + 5]), w3 = pack_bf16x2(x[r0 + 6], x[r0 + 7]);
-      float r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.f, false);
-      r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, r, false);
-      r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, r, false);
-      rs4[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, r, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, l, false);
       pb[q] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
     }
-    l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+    l_run = l;
   };
 
   // O^T += V^T P^T, four 16-key steps; k-step t uses pb[t] = registers 8*(t&1)..+7 of the
@@ -438,9 +443,9 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   f32x16 s_a[2], s_b[2];
   bf16x8 pb[4];
   float mx;
-  dload(krsrc, KSLOT0, j0 * C::BN);
-  dload(vrsrc, VSLOT0, j0 * C::BN);
-  if (j0 + 1 < j1) dload(krsrc, KSLOT0 + C::BLKB, (j0 + 1) * C::BN);
+  dload(kbase, KSLOT0, j0 * C::BN);
+  dload(vbase, VSLOT0, j0 * C::BN);
+  if (j0 + 1 < j1) dload(kbase, KSLOT0 + C::BLKB, (j0 + 1) * C::BN);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   qk(KSLOT0, s_a);
@@ -449,8 +454,8 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
 
   // PAR = (j - j0) & 1 is a literal at every call, so after inlining the slot offsets fold.
   auto step = [&](int j, const int PAR, f32x16* s_cur, f32x16* s_nxt) {
-    if (j + 2 < j1) dload(krsrc, KSLOT0 + PAR * C::BLKB, (j + 2) * C::BN);
-    dload(vrsrc, VSLOT0 + (1 - PAR) * C::BLKB, (j + 1) * C::BN);
+    if (j + 2 < j1) dload(kbase, KSLOT0 + PAR * C::BLKB, (j + 2) * C::BN);
+    dload(vbase, VSLOT0 + (1 - PAR) * C::BLKB, (j + 1) * C::BN);
     rescale_to(mx);
     qk(KSLOT0 + (1 - PAR) * C::BLKB, s_nxt);
     exp_pack(s_cur, pb);
