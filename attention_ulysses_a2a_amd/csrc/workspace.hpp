@@ -28,8 +28,9 @@ SplitPlan choose_split(int n_tiles, int nkv, int D, size_t partial_bytes_per_uni
 // alike: the older one (lower slot) keeps most of the issue slots.  Measured per-block
 // rates relative to a lone workgroup (MI355X, D = 128): older sharer 0.864, younger sharer
 // 0.58.  The table assigns every workgroup a (tile, split, key-block range) so that each
-// tile mixes these classes and each split's range is proportional to its rate: the splits
-// of a tile then finish together and no tile waits on an all-younger-sharer group.  Only
+// tile mixes these classes and its blocks are shared out to minimise the time its slowest
+// split needs (blocks / rate): the splits of a tile then finish together and no tile waits
+// on an all-younger-sharer group.  Only
 // speed depends on this; any table that partitions every tile's keys is correct.
 constexpr int kUnitTableCap = 512;
 struct UnitTable {
