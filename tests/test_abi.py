@@ -191,7 +191,7 @@ def test_schedule_mixes_placements_in_one_round(L):
     i sits at slot i // 8 of XCD i % 8, slots 0..21 share a CU with slots 32..53 (the
     younger, slower partner) and 22..31 run alone.  No tile may be all younger partners, and
     a younger partner never gets more keys than an older partner or a lone workgroup of
-    its tile."""
+    its tile; each tile's blocks are shared out min-max optimally."""
     tile, split, j0, j1 = (np.array(a) for a in xs.xstage_attn_a2a_schedule(1, 4608, 3, 128))
     blocks = j1 - j0
     slot = np.arange(len(tile)) // 8
@@ -202,6 +202,17 @@ def test_schedule_mixes_placements_in_one_round(L):
         assert not young[idx].all()
         if young[idx].any() and (~young[idx]).any():
             assert blocks[idx][young[idx]].max() <= blocks[idx][~young[idx]].min()
+    # Within a tile the blocks are shared out min-max optimally for the placement rates the
+    # table assumes (lone 1.0, older sharer 0.864, younger sharer 0.58): no block can move
+    # off the tile's slowest split (largest blocks / rate) to another split without that
+    # split becoming at least as slow.
+    rate = np.where(slot < 22, 0.864, np.where(slot < 32, 1.0, 0.58))
+    for t in range(tile.max() + 1):
+        idx = np.where(tile == t)[0]
+        tt = blocks[idx] / rate[idx]
+        worst = tt.max()
+        others = np.arange(len(idx)) != np.argmax(tt)
+        assert np.all((blocks[idx][others] + 1) / rate[idx][others] >= worst - 1e-12), t
     # multi-round launches keep equal ranges (the last split may be shorter)
     tile, split, j0, j1 = (np.array(a) for a in xs.xstage_attn_a2a_schedule(1, 16896, 3, 128))
     assert len(set((j1 - j0)[j1 < (16896 + 63) // 64].tolist())) == 1
