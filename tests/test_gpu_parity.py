@@ -203,6 +203,33 @@ def test_largest_supported_tensor():
     assert np.array_equal(g.slabs_host(), oracle.ulysses_scatter(v_host, P))
 
 
+def test_split_counters_reset_between_shapes():
+    """Every launch leaves the key-split arrival counters at zero: launches of shapes with
+    different tile and split counts, issued back to back on one stream with no
+    synchronisation between them, write the same bits as each shape run alone."""
+    shapes = [Workload("ctr-a", 1, 4608, 3, 128, 8, seed=31),   # one-round launch, placement table
+              Workload("ctr-b", 1, 2304, 3, 128, 8, seed=32),
+              Workload("ctr-c", 2, 1000, 2, 64, 8, seed=33)]
+    splits = [xs.xstage_attn_a2a_plan(w.B, w.S, w.H, w.D)[1] for w in shapes]
+    log(f"split counters: key splits per shape {splits}")
+    assert all(n > 1 for n in splits)  # every shape merges through the counters (108, 54, 32 tiles)
+    ins, alone = [], []
+    for w in shapes:
+        qb, kb, vb = make_inputs(w)
+        ins.append(tuple(to_dev(x) for x in (qb, kb, vb)))
+        alone.append(run_fused(w, qb, kb, vb, w.scale).slabs_host())
+    outs = []
+    for rep in range(3):
+        for w, (q, k, v) in zip(shapes, ins):
+            g = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
+            xs.xstage_attn_a2a_fwd(q, k, v, g.views, w.scale)
+            outs.append(g)
+    torch.cuda.synchronize()
+    for i, g in enumerate(outs):
+        assert g.guards_intact()
+        assert np.array_equal(g.slabs_host(), alone[i % len(shapes)]), (i, shapes[i % len(shapes)].name)
+
+
 def test_attn_fwd_contiguous_matches_oracle():
     w = workload("tiny")
     qb, kb, vb = make_inputs(w)
