@@ -220,10 +220,9 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   // K/V blocks go from global memory straight into LDS (buffer_load_dwordx4 ... lds: no
   // registers).  One instruction of wave w fills the 1 KiB LDS segment (i*4 + w) of a
   // block, lane by lane, so each lane fetches the global chunk that belongs at its LDS slot
-  // under the swizzle.  The buffer resource spans the S rows of this (b, h); a lane's
-  // offset is its fixed offset within a block plus the block's, all in the per-lane
-  // offset (the scalar offset stays 0, so the range check sees the whole offset): rows
-  // past the end of the sequence read as zeros — no clamping, no branches.
+  // under the swizzle.  The range check covers the per-lane offset (the scalar offset
+  // stays 0), and a resource ends where the head's S rows end: rows past the end of the
+  // sequence read as zeros — no clamping, no branches.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t head_bytes = (uint32_t)kv_rows * rs * 2u;  // one K/V buffer's rows of this head
   auto make_rsrc = [&](const uint16_t* base) {
