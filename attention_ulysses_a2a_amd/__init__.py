@@ -16,6 +16,7 @@ import math
 
 from ._lib import (  # noqa: F401
     LIB_PATH,
+    WS_FULL,
     XSTAGE_ERR_HIP,
     XSTAGE_ERR_INVALID,
     XSTAGE_ERR_UNSUPPORTED,
@@ -32,6 +33,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "xstage_attn_a2a_fwd",
+    "xstage_attn_split_ws_size",
+    "split_workspace",
     "xstage_attn_fwd",
     "xstage_a2a_scatter",
     "xstage_attn_a2a_unfused",
@@ -62,17 +65,24 @@ def _check(status: int, where: str) -> None:
         raise XStageError(status, where)
 
 
-def _dev_tensor(t, name: str):
+def _dev_tensor(t, name: str, device=None, min_bytes=None, bf16=True):
+    """Checks that ``t`` is a contiguous device tensor (bf16 storage unless bf16=False), on
+    ``device`` if given, holding at least ``min_bytes`` bytes if given.  The C ABI sees only
+    pointers, so the sizes and devices of the buffers it writes are checked here."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if t.element_size() != 2 or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+    if bf16 and (t.element_size() != 2 or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16)):
         raise ValueError(f"{name} must hold bf16 values (bfloat16 or 16-bit integer storage)")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the call writes {min_bytes}")
     return t
 
 
@@ -84,63 +94,264 @@ def _stream_of(t, stream):
     return getattr(stream, "cuda_stream", stream)
 
 
-def _slab_ptrs(out_slabs):
+def _split_ws(split_ws, device):
+    """(pointer, bytes) of an optional split workspace (any dtype, contiguous, on ``device``)."""
+    if split_ws is None:
+        return None, 0
+    _dev_tensor(split_ws, "split_ws", device=device, bf16=False)
+    return split_ws.data_ptr(), split_ws.numel() * split_ws.element_size()
+
+
+def _slab_ptrs(out_slabs, device=None, slab_bytes=None):
+    """Device pointers of P destination buffers, given as a list of tensors or one tensor whose
+    leading index selects the destination; each must hold ``slab_bytes(P)`` bytes."""
     import torch
 
     if isinstance(out_slabs, torch.Tensor):
-        _dev_tensor(out_slabs, "out_slabs")
-        return [out_slabs[p].data_ptr() for p in range(out_slabs.shape[0])], out_slabs.shape[0]
+        _dev_tensor(out_slabs, "out_slabs", device=device)
+        P = int(out_slabs.shape[0])
+        need = slab_bytes(P) if slab_bytes else None
+        if need is not None:
+            _dev_tensor(out_slabs, "out_slabs", min_bytes=need * P)
+        return [out_slabs[p].data_ptr() for p in range(P)], P
     slabs = list(out_slabs)
-    for i, s in enumerate(slabs):
-        _dev_tensor(s, f"out_slabs[{i}]")
-    return [s.data_ptr() for s in slabs], len(slabs)
+    P = len(slabs)
+    need = slab_bytes(P) if (slab_bytes and P) else None
+    for i, t in enumerate(slabs):
+        _dev_tensor(t, f"out_slabs[{i}]", device=device, min_bytes=need)
+    return [t.data_ptr() for t in slabs], P
 
 
-def _shards(x, name):
+def _shards(x, name, device=None):
     """Device pointers and the common [B, S/P, H, D] shape of P shards, given as a list of
     tensors or one [P, B, S/P, H, D] tensor."""
     import torch
 
     if isinstance(x, torch.Tensor):
-        _dev_tensor(x, name)
+        _dev_tensor(x, name, device=device)
         if x.dim() != 5:
             raise ValueError(f"{name} must be [P, B, S/P, H, D]")
         return [x[p].data_ptr() for p in range(x.shape[0])], tuple(int(d) for d in x.shape[1:])
-    xs = list(x)
-    if not xs:
+    xs_ = list(x)
+    if not xs_:
         raise ValueError(f"{name} is empty")
-    for i, t in enumerate(xs):
-        _dev_tensor(t, f"{name}[{i}]")
-        if t.dim() != 4 or t.shape != xs[0].shape:
+    for i, t in enumerate(xs_):
+        _dev_tensor(t, f"{name}[{i}]", device=device)
+        if t.dim() != 4 or t.shape != xs_[0].shape:
             raise ValueError(f"{name} must be P tensors of one [B, S/P, H, D] shape")
-    return [t.data_ptr() for t in xs], tuple(int(d) for d in xs[0].shape)
+    return [t.data_ptr() for t in xs_], tuple(int(d) for d in xs_[0].shape)
 
 
-def _strided_call(q, k, v, out_dst, h_dst0, scale, stream):
+def _qkv(q, k, v):
+    _dev_tensor(q, "q")
+    _dev_tensor(k, "k", device=q.device)
+    _dev_tensor(v, "v", device=q.device)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, S, H_local, D] shape")
+    return tuple(int(x) for x in q.shape)
+
+
+def _scale(scale, D):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def _slab_need(B, S, H, D):
+    """Bytes of one of P slabs [B, S/P, H, D] (None when S % P != 0: the library rejects it)."""
+    return lambda P: (B * (S // P) * H * D * 2) if P > 0 and S % P == 0 else None
+
+
+# ---- marshalling: one function per entry point, shared by the calls and by bind() -------
+# Each returns (C arguments, objects to keep alive during the call, device).
+
+def _m_attn_a2a_fwd(q, k, v, out_slabs, scale=None, split_ws=None, stream=None):
     B, S, H, D = _qkv(q, k, v)
-    ptrs, shp = _shards(out_dst, "out_dst")
+    ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
+    arr, keep = ptr_array(ptrs)
+    ws, wsb = _split_ws(split_ws, q.device)
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), ws, wsb,
+            _stream_of(q, stream))
+    return call, (q, k, v, out_slabs, keep, split_ws), q.device
+
+
+def _m_attn_fwd(q, k, v, out, scale=None, split_ws=None, stream=None):
+    B, S, H, D = _qkv(q, k, v)
+    _dev_tensor(out, "out", device=q.device, min_bytes=B * S * H * D * 2)
+    ws, wsb = _split_ws(split_ws, q.device)
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, H, D, _scale(scale, D), ws, wsb,
+            _stream_of(q, stream))
+    return call, (q, k, v, out, split_ws), q.device
+
+
+def _m_a2a_scatter(inp, out_slabs, stream=None):
+    _dev_tensor(inp, "in")
+    B, S, H, D = (int(x) for x in inp.shape)
+    ptrs, P = _slab_ptrs(out_slabs, inp.device, _slab_need(B, S, H, D))
+    arr, keep = ptr_array(ptrs)
+    return (inp.data_ptr(), arr, B, S, H, D, P, _stream_of(inp, stream)), (inp, out_slabs, keep), inp.device
+
+
+def _m_attn_a2a_unfused(q, k, v, workspace, out_slabs, scale=None, split_ws=None, stream=None):
+    B, S, H, D = _qkv(q, k, v)
+    _dev_tensor(workspace, "workspace", device=q.device, min_bytes=B * S * H * D * 2)
+    ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
+    arr, keep = ptr_array(ptrs)
+    ws, wsb = _split_ws(split_ws, q.device)
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), workspace.data_ptr(), arr, B, S, H, D, P, _scale(scale, D),
+            ws, wsb, _stream_of(q, stream))
+    return call, (q, k, v, workspace, out_slabs, keep, split_ws), q.device
+
+
+def _m_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, split_ws=None, stream=None):
+    B, S, H, D = _qkv(q, k, v)
+    ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
+    ws, wsb = _split_ws(split_ws, q.device)
+    nwg, _ = xstage_attn_a2a_plan(B, S, H, D, wsb)
+    _dev_tensor(stamps, "stamps", device=q.device, min_bytes=nwg * 16 * 8, bf16=False)
+    if stamps.element_size() != 8:
+        raise ValueError("stamps must be a 64-bit tensor")
+    arr, keep = ptr_array(ptrs)
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), int(mode),
+            stamps.data_ptr(), ws, wsb, _stream_of(q, stream))
+    return call, (q, k, v, out_slabs, stamps, keep, split_ws), q.device
+
+
+def _m_attn_a2a_fwd_strided(q, k, v, out_dst, h_dst0, scale=None, split_ws=None, stream=None):
+    B, S, H, D = _qkv(q, k, v)
+    ptrs, shp = _shards(out_dst, "out_dst", device=q.device)
     P = len(ptrs)
     if shp[0] != B or shp[1] * P != S or shp[3] != D:
         raise ValueError("out_dst must be P buffers of [B, S/P, H_dst, D]")
     arr, keep = ptr_array(ptrs)
-    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, shp[2], int(h_dst0), _scale(scale, D),
-            _stream_of(q, stream)), keep
+    ws, wsb = _split_ws(split_ws, q.device)
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, shp[2], int(h_dst0), _scale(scale, D),
+            ws, wsb, _stream_of(q, stream))
+    return call, (q, k, v, out_dst, keep, split_ws), q.device
 
 
-def _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream):
+def _ulysses_common(q_src, k_src, v_src, out_dst):
     qp, shp = _shards(q_src, "q_src")
-    kp, kshp = _shards(k_src, "k_src")
-    vp, vshp = _shards(v_src, "v_src")
-    op, oshp = _shards(out_dst, "out_dst")
+    t0 = q_src if not isinstance(q_src, (list, tuple)) else q_src[0]
+    dev = t0.device
+    kp, kshp = _shards(k_src, "k_src", device=dev)
+    vp, vshp = _shards(v_src, "v_src", device=dev)
+    op, oshp = _shards(out_dst, "out_dst", device=dev)
     P = len(qp)
     if not (len(kp) == len(vp) == len(op) == P and kshp == vshp == oshp == shp):
         raise ValueError("q_src, k_src, v_src, out_dst must be P shards of one [B, S/P, H, D] shape")
-    B, sp, H, D = shp
     arrs = [ptr_array(x) for x in (qp, kp, vp, op)]
-    t0 = q_src if not isinstance(q_src, (list, tuple)) else q_src[0]
+    return arrs, shp, P, t0, dev
+
+
+def _m_ulysses_attn_fwd(q_src, k_src, v_src, out_dst, H_local, h0, scale=None, split_ws=None, stream=None):
+    arrs, (B, sp, H, D), P, t0, dev = _ulysses_common(q_src, k_src, v_src, out_dst)
+    ws, wsb = _split_ws(split_ws, dev)
     call = (arrs[0][0], arrs[1][0], arrs[2][0], arrs[3][0], B, sp * P, H, int(H_local), int(h0), D, P,
-            _scale(scale, D), _stream_of(t0, stream))
-    return call, [a[1] for a in arrs], t0.device
+            _scale(scale, D), ws, wsb, _stream_of(t0, stream))
+    return call, (q_src, k_src, v_src, out_dst, [a[1] for a in arrs], split_ws), dev
+
+
+def _ulysses_ws_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, split_ws, stream, n_tensors):
+    arrs, (B, sp, H, D), P, t0, dev = _ulysses_common(q_src, k_src, v_src, out_dst)
+    _dev_tensor(workspace, "workspace", device=dev, min_bytes=n_tensors * B * sp * P * int(H_local) * D * 2)
+    ws, wsb = _split_ws(split_ws, dev)
+    call = (arrs[0][0], arrs[1][0], arrs[2][0], workspace.data_ptr(), arrs[3][0], B, sp * P, H, int(H_local),
+            int(h0), D, P, _scale(scale, D), ws, wsb, _stream_of(t0, stream))
+    return call, (q_src, k_src, v_src, workspace, out_dst, [a[1] for a in arrs], split_ws), dev
+
+
+def _m_ulysses_attn_unfused(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=None, split_ws=None,
+                            stream=None):
+    return _ulysses_ws_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, split_ws, stream, 4)
+
+
+def _m_ulysses_attn_fwd_kv_staged(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=None,
+                                  split_ws=None, stream=None):
+    return _ulysses_ws_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, split_ws, stream, 2)
+
+
+_MARSHAL = {
+    "xstage_attn_a2a_fwd": _m_attn_a2a_fwd,
+    "xstage_attn_fwd": _m_attn_fwd,
+    "xstage_a2a_scatter": _m_a2a_scatter,
+    "xstage_attn_a2a_unfused": _m_attn_a2a_unfused,
+    "xstage_attn_a2a_fwd_traced": _m_attn_a2a_fwd_traced,
+    "xstage_attn_a2a_fwd_strided": _m_attn_a2a_fwd_strided,
+    "xstage_ulysses_attn_fwd": _m_ulysses_attn_fwd,
+    "xstage_ulysses_attn_unfused": _m_ulysses_attn_unfused,
+    "xstage_ulysses_attn_fwd_kv_staged": _m_ulysses_attn_fwd_kv_staged,
+}
+
+
+def _invoke(name, *args, **kwargs) -> None:
+    import torch
+
+    call, keep, dev = _MARSHAL[name](*args, **kwargs)
+    with torch.cuda.device(dev):
+        st = getattr(lib(), name)(*call)
+    del keep
+    _check(st, name)
+
+
+def xstage_attn_a2a_fwd(q, k, v, out_slabs, scale=None, split_ws=None, stream=None) -> None:
+    """Fused attention + all-to-all scatter into the P slabs (a list of P tensors
+    [B, S/P, H_local, D] or one [P, B, S/P, H_local, D] tensor); ``split_ws``: optional
+    caller-owned split workspace (``split_workspace``); see include/xstage.h."""
+    _invoke("xstage_attn_a2a_fwd", q, k, v, out_slabs, scale=scale, split_ws=split_ws, stream=stream)
+
+
+def xstage_attn_fwd(q, k, v, out, scale=None, split_ws=None, stream=None) -> None:
+    """Attention into a contiguous [B, S, H_local, D] output (first half of the serial path)."""
+    _invoke("xstage_attn_fwd", q, k, v, out, scale=scale, split_ws=split_ws, stream=stream)
+
+
+def xstage_a2a_scatter(inp, out_slabs, stream=None) -> None:
+    """Separate all-to-all send step: contiguous [B, S, H_local, D] -> P slabs."""
+    _invoke("xstage_a2a_scatter", inp, out_slabs, stream=stream)
+
+
+def xstage_attn_a2a_unfused(q, k, v, workspace, out_slabs, scale=None, split_ws=None, stream=None) -> None:
+    """Serial baseline: attention into ``workspace`` ([B, S, H_local, D] bf16) then the separate
+    scatter."""
+    _invoke("xstage_attn_a2a_unfused", q, k, v, workspace, out_slabs, scale=scale, split_ws=split_ws, stream=stream)
+
+
+def xstage_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, split_ws=None, stream=None) -> None:
+    """Instrumented fused call (store-span study); ``stamps`` is an int64 device tensor of
+    n_workgroups * 16 entries (xstage_attn_a2a_plan with the same workspace); modes as in
+    include/xstage.h."""
+    _invoke("xstage_attn_a2a_fwd_traced", q, k, v, out_slabs, mode, stamps, scale=scale, split_ws=split_ws,
+            stream=stream)
+
+
+def xstage_attn_a2a_fwd_strided(q, k, v, out_dst, h_dst0, scale=None, split_ws=None, stream=None) -> None:
+    """Fused call writing head columns [h_dst0, h_dst0 + H_local) of full-head receive
+    buffers out_dst (P x [B, S/P, H_dst, D]); see include/xstage.h."""
+    _invoke("xstage_attn_a2a_fwd_strided", q, k, v, out_dst, h_dst0, scale=scale, split_ws=split_ws, stream=stream)
+
+
+def xstage_ulysses_attn_fwd(q_src, k_src, v_src, out_dst, H_local, h0, scale=None, split_ws=None,
+                            stream=None) -> None:
+    """One rank's Ulysses attention layer: heads [h0, h0 + H_local) read from the P sequence
+    shards (P x [B, S/P, H, D] each) and written into the P receive buffers; see
+    include/xstage.h."""
+    _invoke("xstage_ulysses_attn_fwd", q_src, k_src, v_src, out_dst, H_local, h0, scale=scale, split_ws=split_ws,
+            stream=stream)
+
+
+def xstage_ulysses_attn_unfused(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=None, split_ws=None,
+                                stream=None) -> None:
+    """Serial Ulysses layer: separate gather, attention, separate strided scatter;
+    ``workspace`` holds 4 x [B, S, H_local, D] bf16."""
+    _invoke("xstage_ulysses_attn_unfused", q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=scale,
+            split_ws=split_ws, stream=stream)
+
+
+def xstage_ulysses_attn_fwd_kv_staged(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=None,
+                                      split_ws=None, stream=None) -> None:
+    """Ulysses layer with K and V gathered into ``workspace`` (2 x [B, S, H_local, D] bf16)
+    and Q read from the shards in place; same output as xstage_ulysses_attn_fwd."""
+    _invoke("xstage_ulysses_attn_fwd_kv_staged", q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=scale,
+            split_ws=split_ws, stream=stream)
 
 
 def xstage_ulysses_gather(src_shards, out, H_local, h0, stream=None) -> None:
@@ -149,8 +360,8 @@ def xstage_ulysses_gather(src_shards, out, H_local, h0, stream=None) -> None:
     import torch
 
     ptrs, (B, sp, H, D) = _shards(src_shards, "src_shards")
-    _dev_tensor(out, "out")
     P = len(ptrs)
+    _dev_tensor(out, "out", min_bytes=B * sp * P * int(H_local) * D * 2)
     arr, keep = ptr_array(ptrs)
     with torch.cuda.device(out.device):
         st = lib().xstage_ulysses_gather(arr, out.data_ptr(), B, sp * P, H, int(H_local), int(h0), D, P,
@@ -165,8 +376,10 @@ def xstage_a2a_scatter_strided(inp, out_dst, h_dst0, stream=None) -> None:
 
     _dev_tensor(inp, "in")
     B, S, H, D = (int(x) for x in inp.shape)
-    ptrs, shp = _shards(out_dst, "out_dst")
+    ptrs, shp = _shards(out_dst, "out_dst", device=inp.device)
     P = len(ptrs)
+    if shp[0] != B or shp[1] * P != S or shp[3] != D:
+        raise ValueError("out_dst must be P buffers of [B, S/P, H_dst, D]")
     arr, keep = ptr_array(ptrs)
     with torch.cuda.device(inp.device):
         st = lib().xstage_a2a_scatter_strided(inp.data_ptr(), arr, B, S, H, D, P, shp[2], int(h_dst0),
@@ -175,165 +388,46 @@ def xstage_a2a_scatter_strided(inp, out_dst, h_dst0, stream=None) -> None:
     _check(st, "xstage_a2a_scatter_strided")
 
 
-def _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream):
-    call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
-    _dev_tensor(workspace, "workspace")
-    # (q, k, v, out, B, S, H, H_local, h0, D, P, scale, stream) -> insert the workspace
-    call = call[:3] + (workspace.data_ptr(),) + call[3:]
-    return call, keep + [workspace], dev
+def xstage_attn_split_ws_size(B: int, S: int, H_local: int, D: int) -> int:
+    """Bytes of split workspace the attention entry points use for this shape at full speed
+    (0 when the shape is not split)."""
+    n = ctypes.c_ulonglong(0)
+    _check(lib().xstage_attn_split_ws_size(int(B), int(S), int(H_local), int(D), ctypes.byref(n)),
+           "xstage_attn_split_ws_size")
+    return n.value
 
 
-def xstage_ulysses_attn_unfused(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=None, stream=None) -> None:
-    """Serial Ulysses layer: separate gather, attention, separate strided scatter;
-    ``workspace`` holds 4 x [B, S, H_local, D] bf16."""
+def split_workspace(B: int, S: int, H_local: int, D: int, device=None):
+    """A zero-filled split workspace for this shape (torch uint8 device tensor), or None when
+    the shape is not split.  Allocation is the caller's (torch's), never the library's."""
     import torch
 
-    call, keep, dev = _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream)
-    with torch.cuda.device(dev):
-        st = lib().xstage_ulysses_attn_unfused(*call)
-    del keep
-    _check(st, "xstage_ulysses_attn_unfused")
+    n = xstage_attn_split_ws_size(B, S, H_local, D)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device if device is not None else "cuda")
 
 
-def xstage_ulysses_attn_fwd_kv_staged(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale=None,
-                                      stream=None) -> None:
-    """Ulysses layer with K and V gathered into ``workspace`` (2 x [B, S, H_local, D] bf16)
-    and Q read from the shards in place; same output as xstage_ulysses_attn_fwd."""
-    import torch
-
-    call, keep, dev = _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream)
-    with torch.cuda.device(dev):
-        st = lib().xstage_ulysses_attn_fwd_kv_staged(*call)
-    del keep
-    _check(st, "xstage_ulysses_attn_fwd_kv_staged")
-
-
-def xstage_attn_a2a_fwd_strided(q, k, v, out_dst, h_dst0, scale=None, stream=None) -> None:
-    """Fused call writing head columns [h_dst0, h_dst0 + H_local) of full-head receive
-    buffers out_dst (P x [B, S/P, H_dst, D]); see include/xstage.h."""
-    import torch
-
-    call, keep = _strided_call(q, k, v, out_dst, h_dst0, scale, stream)
-    with torch.cuda.device(q.device):
-        st = lib().xstage_attn_a2a_fwd_strided(*call)
-    del keep
-    _check(st, "xstage_attn_a2a_fwd_strided")
-
-
-def xstage_ulysses_attn_fwd(q_src, k_src, v_src, out_dst, H_local, h0, scale=None, stream=None) -> None:
-    """One rank's Ulysses attention layer: heads [h0, h0 + H_local) read from the P sequence
-    shards (P x [B, S/P, H, D] each) and written into the P receive buffers; see
-    include/xstage.h."""
-    import torch
-
-    call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
-    with torch.cuda.device(dev):
-        st = lib().xstage_ulysses_attn_fwd(*call)
-    del keep
-    _check(st, "xstage_ulysses_attn_fwd")
-
-
-def _qkv(q, k, v):
-    _dev_tensor(q, "q"), _dev_tensor(k, "k"), _dev_tensor(v, "v")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [B, S, H_local, D] shape")
-    return tuple(int(x) for x in q.shape)
-
-
-def _scale(scale, D):
-    return 1.0 / math.sqrt(D) if scale is None else float(scale)
-
-
-def xstage_attn_a2a_fwd(q, k, v, out_slabs, scale=None, stream=None) -> None:
-    """Fused attention + all-to-all scatter; see xstage_attn_a2a_fwd in include/xstage.h."""
-    import torch
-
-    B, S, H, D = _qkv(q, k, v)
-    ptrs, P = _slab_ptrs(out_slabs)
-    arr, keep = ptr_array(ptrs)
-    with torch.cuda.device(q.device):
-        st = lib().xstage_attn_a2a_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P,
-                                       _scale(scale, D), _stream_of(q, stream))
-    del keep
-    _check(st, "xstage_attn_a2a_fwd")
-
-
-def xstage_attn_fwd(q, k, v, out, scale=None, stream=None) -> None:
-    """Attention into a contiguous [B, S, H_local, D] output (first half of the serial path)."""
-    import torch
-
-    B, S, H, D = _qkv(q, k, v)
-    _dev_tensor(out, "out")
-    with torch.cuda.device(q.device):
-        st = lib().xstage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, H, D,
-                                   _scale(scale, D), _stream_of(q, stream))
-    _check(st, "xstage_attn_fwd")
-
-
-def xstage_a2a_scatter(inp, out_slabs, stream=None) -> None:
-    """Separate all-to-all send step: contiguous [B, S, H_local, D] -> P slabs."""
-    import torch
-
-    _dev_tensor(inp, "in")
-    B, S, H, D = (int(x) for x in inp.shape)
-    ptrs, P = _slab_ptrs(out_slabs)
-    arr, keep = ptr_array(ptrs)
-    with torch.cuda.device(inp.device):
-        st = lib().xstage_a2a_scatter(inp.data_ptr(), arr, B, S, H, D, P, _stream_of(inp, stream))
-    del keep
-    _check(st, "xstage_a2a_scatter")
-
-
-def xstage_attn_a2a_unfused(q, k, v, workspace, out_slabs, scale=None, stream=None) -> None:
-    """Serial baseline: attention into ``workspace`` then the separate scatter."""
-    import torch
-
-    B, S, H, D = _qkv(q, k, v)
-    _dev_tensor(workspace, "workspace")
-    ptrs, P = _slab_ptrs(out_slabs)
-    arr, keep = ptr_array(ptrs)
-    with torch.cuda.device(q.device):
-        st = lib().xstage_attn_a2a_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), workspace.data_ptr(), arr,
-                                           B, S, H, D, P, _scale(scale, D), _stream_of(q, stream))
-    del keep
-    _check(st, "xstage_attn_a2a_unfused")
-
-
-def xstage_attn_a2a_plan(B: int, S: int, H_local: int, D: int):
-    """(n_workgroups, n_split) of the attention launch for this shape on the current device."""
+def xstage_attn_a2a_plan(B: int, S: int, H_local: int, D: int, split_ws_bytes=None):
+    """(n_workgroups, n_split) of the attention launch for this shape on the current device
+    given ``split_ws_bytes`` of split workspace (None: as much as the fastest plan uses)."""
     nwg, nsp = ctypes.c_int(0), ctypes.c_int(0)
-    _check(lib().xstage_attn_a2a_plan(int(B), int(S), int(H_local), int(D), ctypes.byref(nwg), ctypes.byref(nsp)),
-           "xstage_attn_a2a_plan")
+    wsb = WS_FULL if split_ws_bytes is None else int(split_ws_bytes)
+    _check(lib().xstage_attn_a2a_plan(int(B), int(S), int(H_local), int(D), wsb, ctypes.byref(nwg),
+                                      ctypes.byref(nsp)), "xstage_attn_a2a_plan")
     return nwg.value, nsp.value
 
 
-def xstage_attn_a2a_schedule(B: int, S: int, H_local: int, D: int):
+def xstage_attn_a2a_schedule(B: int, S: int, H_local: int, D: int, split_ws_bytes=None):
     """Per-workgroup (tile, split, j0, j1) of the attention launch for this shape on the
     current device, as four lists (key blocks of 64 in [j0, j1))."""
-    nwg, _ = xstage_attn_a2a_plan(B, S, H_local, D)
+    nwg, _ = xstage_attn_a2a_plan(B, S, H_local, D, split_ws_bytes)
+    wsb = WS_FULL if split_ws_bytes is None else int(split_ws_bytes)
     arrs = [(ctypes.c_int * max(nwg, 1))() for _ in range(4)]
     n = ctypes.c_int(0)
-    _check(lib().xstage_attn_a2a_schedule(int(B), int(S), int(H_local), int(D), nwg, *arrs, ctypes.byref(n)),
+    _check(lib().xstage_attn_a2a_schedule(int(B), int(S), int(H_local), int(D), wsb, nwg, *arrs, ctypes.byref(n)),
            "xstage_attn_a2a_schedule")
     return tuple(list(a)[: n.value] for a in arrs)
-
-
-def xstage_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, stream=None) -> None:
-    """Instrumented fused call (store-span study); ``stamps`` is an int64 device tensor of
-    n_workgroups * 16 entries (xstage_attn_a2a_plan); modes as in include/xstage.h."""
-    import torch
-
-    B, S, H, D = _qkv(q, k, v)
-    ptrs, P = _slab_ptrs(out_slabs)
-    nwg, _ = xstage_attn_a2a_plan(B, S, H, D)
-    if not stamps.is_cuda or stamps.element_size() != 8 or stamps.numel() < nwg * 16 or not stamps.is_contiguous():
-        raise ValueError(f"stamps must be a contiguous 64-bit device tensor of >= {nwg * 16} entries")
-    arr, keep = ptr_array(ptrs)
-    with torch.cuda.device(q.device):
-        st = lib().xstage_attn_a2a_fwd_traced(q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P,
-                                              _scale(scale, D), int(mode), stamps.data_ptr(), _stream_of(q, stream))
-    del keep
-    _check(st, "xstage_attn_a2a_fwd_traced")
 
 
 def _int_array(vals):
@@ -453,74 +547,17 @@ def bind(name: str, *args, **kwargs) -> _Bound:
     would otherwise cost about as much host time as a short kernel takes on the GPU.  The
     bound buffers are kept alive by the callable; the stream is fixed at bind time (the
     current stream of the tensors' device unless ``stream`` is given), and the calls must be
-    made with that device current.  Supported: xstage_attn_a2a_fwd, xstage_attn_fwd,
-    xstage_a2a_scatter, xstage_attn_a2a_unfused, xstage_attn_a2a_fwd_traced,
-    xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd, xstage_ulysses_attn_unfused,
-    xstage_ulysses_attn_fwd_kv_staged, xstage_moe_waves_run, with the same arguments as the
-    functions.
+    made with that device current.  Supported: the attention entry points
+    (xstage_attn_a2a_fwd, xstage_attn_fwd, xstage_a2a_scatter, xstage_attn_a2a_unfused,
+    xstage_attn_a2a_fwd_traced, xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd,
+    xstage_ulysses_attn_unfused, xstage_ulysses_attn_fwd_kv_staged) and
+    xstage_moe_waves_run, with the same arguments as the functions.
     """
     import torch
 
     L = lib()
-    if name == "xstage_attn_a2a_fwd":
-        q, k, v, out_slabs = args[:4]
-        scale, stream = kwargs.get("scale", args[4] if len(args) > 4 else None), kwargs.get("stream")
-        B, S, H, D = _qkv(q, k, v)
-        ptrs, P = _slab_ptrs(out_slabs)
-        arr, keep = ptr_array(ptrs)
-        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), _stream_of(q, stream))
-        refs, dev = (q, k, v, out_slabs, keep), q.device
-    elif name == "xstage_attn_fwd":
-        q, k, v, out = args[:4]
-        scale, stream = kwargs.get("scale", args[4] if len(args) > 4 else None), kwargs.get("stream")
-        B, S, H, D = _qkv(q, k, v)
-        _dev_tensor(out, "out")
-        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, H, D, _scale(scale, D),
-                _stream_of(q, stream))
-        refs, dev = (q, k, v, out), q.device
-    elif name == "xstage_a2a_scatter":
-        inp, out_slabs = args[:2]
-        stream = kwargs.get("stream")
-        _dev_tensor(inp, "in")
-        B, S, H, D = (int(x) for x in inp.shape)
-        ptrs, P = _slab_ptrs(out_slabs)
-        arr, keep = ptr_array(ptrs)
-        call = (inp.data_ptr(), arr, B, S, H, D, P, _stream_of(inp, stream))
-        refs, dev = (inp, out_slabs, keep), inp.device
-    elif name == "xstage_attn_a2a_unfused":
-        q, k, v, workspace, out_slabs = args[:5]
-        scale, stream = kwargs.get("scale", args[5] if len(args) > 5 else None), kwargs.get("stream")
-        B, S, H, D = _qkv(q, k, v)
-        _dev_tensor(workspace, "workspace")
-        ptrs, P = _slab_ptrs(out_slabs)
-        arr, keep = ptr_array(ptrs)
-        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), workspace.data_ptr(), arr, B, S, H, D, P,
-                _scale(scale, D), _stream_of(q, stream))
-        refs, dev = (q, k, v, workspace, out_slabs, keep), q.device
-    elif name == "xstage_attn_a2a_fwd_traced":
-        q, k, v, out_slabs, mode, stamps = args[:6]
-        scale, stream = kwargs.get("scale", args[6] if len(args) > 6 else None), kwargs.get("stream")
-        B, S, H, D = _qkv(q, k, v)
-        ptrs, P = _slab_ptrs(out_slabs)
-        arr, keep = ptr_array(ptrs)
-        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), int(mode),
-                stamps.data_ptr(), _stream_of(q, stream))
-        refs, dev = (q, k, v, out_slabs, stamps, keep), q.device
-    elif name == "xstage_attn_a2a_fwd_strided":
-        q, k, v, out_dst, h_dst0 = args[:5]
-        scale, stream = kwargs.get("scale", args[5] if len(args) > 5 else None), kwargs.get("stream")
-        call, keep = _strided_call(q, k, v, out_dst, h_dst0, scale, stream)
-        refs, dev = (q, k, v, out_dst, keep), q.device
-    elif name == "xstage_ulysses_attn_fwd":
-        q_src, k_src, v_src, out_dst, H_local, h0 = args[:6]
-        scale, stream = kwargs.get("scale", args[6] if len(args) > 6 else None), kwargs.get("stream")
-        call, keep, dev = _ulysses_call(q_src, k_src, v_src, out_dst, H_local, h0, scale, stream)
-        refs = (q_src, k_src, v_src, out_dst, keep)
-    elif name in ("xstage_ulysses_attn_unfused", "xstage_ulysses_attn_fwd_kv_staged"):
-        q_src, k_src, v_src, workspace, out_dst, H_local, h0 = args[:7]
-        scale, stream = kwargs.get("scale", args[7] if len(args) > 7 else None), kwargs.get("stream")
-        call, keep, dev = _ulysses_unfused_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, stream)
-        refs = (q_src, k_src, v_src, workspace, out_dst, keep)
+    if name in _MARSHAL:
+        call, refs, dev = _MARSHAL[name](*args, **kwargs)
     elif name == "xstage_moe_waves_run":
         x, w1, w2, h, expert_offsets, dst_slab, dst_row, outs, epw, schedule = args[:10]
         stamps, stream = kwargs.get("stamps", args[10] if len(args) > 10 else None), kwargs.get("stream")

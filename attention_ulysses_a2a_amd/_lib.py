@@ -70,21 +70,26 @@ _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _PP = ctypes.POINTER(ctypes.c_void_p)
 
+_u64 = ctypes.c_ulonglong
+_f = ctypes.c_float
+_WS = [_vp, _u64]  # split_ws, split_ws_bytes
+
 SIGNATURES = {
-    "xstage_attn_a2a_fwd": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, ctypes.c_float, _vp]),
-    "xstage_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, ctypes.c_float, _vp]),
+    "xstage_attn_a2a_fwd": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),
+    "xstage_attn_split_ws_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_u64)]),
+    "xstage_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f] + _WS + [_vp]),
     "xstage_a2a_scatter": (_i, [_vp, _PP, _i, _i, _i, _i, _i, _vp]),
-    "xstage_attn_a2a_unfused": (_i, [_vp, _vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, ctypes.c_float, _vp]),
-    "xstage_attn_a2a_fwd_strided": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp]),
-    "xstage_ulysses_attn_fwd": (_i, [_PP, _PP, _PP, _PP, _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp]),
+    "xstage_attn_a2a_unfused": (_i, [_vp, _vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),
+    "xstage_attn_a2a_fwd_strided": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),
+    "xstage_ulysses_attn_fwd": (_i, [_PP, _PP, _PP, _PP, _i, _i, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),
     "xstage_ulysses_gather": (_i, [_PP, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "xstage_a2a_scatter_strided": (_i, [_vp, _PP, _i, _i, _i, _i, _i, _i, _i, _vp]),
-    "xstage_ulysses_attn_unfused": (_i, [_PP, _PP, _PP, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp]),
+    "xstage_ulysses_attn_unfused": (_i, [_PP, _PP, _PP, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),
     "xstage_ulysses_attn_fwd_kv_staged": (
-        _i, [_PP, _PP, _PP, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp]),
-    "xstage_attn_a2a_plan": (_i, [_i, _i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
-    "xstage_attn_a2a_schedule": (_i, [_i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 5),
-    "xstage_attn_a2a_fwd_traced": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp, _vp]),
+        _i, [_PP, _PP, _PP, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),
+    "xstage_attn_a2a_plan": (_i, [_i, _i, _i, _i, _u64, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "xstage_attn_a2a_schedule": (_i, [_i, _i, _i, _i, _u64, _i] + [ctypes.POINTER(_i)] * 5),
+    "xstage_attn_a2a_fwd_traced": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f, _i, _vp] + _WS + [_vp]),
     "xstage_moe_waves_run": (_i, [ctypes.POINTER(MoeParams), _vp]),
     "xstage_moe_waves_plan": (_i, [_i, ctypes.POINTER(_i), _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 4),
     "xstage_burst_gap_run": (_i, [ctypes.POINTER(BGParams), _vp]),
@@ -93,6 +98,9 @@ SIGNATURES = {
     "xstage_bg_pacing_chunks": (_i, [ctypes.c_double] * 6 + [_i, ctypes.POINTER(ctypes.c_double)]),
     "xstage_status_str": (ctypes.c_char_p, [_i]),
 }
+
+# split_ws_bytes value asking the plan queries for the unconstrained (full-speed) plan
+WS_FULL = (1 << 64) - 1
 
 _LIB = None
 

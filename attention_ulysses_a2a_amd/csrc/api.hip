@@ -9,13 +9,16 @@
 #include "common.hpp"
 #include "moe_waves.hpp"
 #include "validate.hpp"
+#include "workspace.hpp"
 
 namespace xstage {
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
-                    int P, float scale, hipStream_t stream, int mode = 0, unsigned long long* stamps = nullptr,
-                    const Layout* layout = nullptr);
-int attn_workgroups(int B, int S, int H, int D, int* n_split);
-int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, int* j0, int* j1);
+                    int P, float scale, void* ws, unsigned long long ws_bytes, hipStream_t stream, int mode = 0,
+                    unsigned long long* stamps = nullptr, const Layout* layout = nullptr);
+int attn_workgroups(int B, int S, int H, int D, unsigned long long ws_bytes, int* n_split);
+unsigned long long attn_ws_used(int B, int S, int H, int D, unsigned long long ws_bytes);
+int attn_schedule(int B, int S, int H, int D, unsigned long long ws_bytes, int cap, int* tile, int* split, int* j0,
+                  int* j1);
 int launch_scatter(const void* in, const SlabTable& slabs, int B, int S, int H, int D, int P, hipStream_t stream);
 int launch_slice_copy(const void* const* src, int src_sharded, int src_w, int src_off, void* const* dst,
                       int dst_sharded, int dst_w, int dst_off, int B, int S, int H_local, int D, int P,
@@ -28,15 +31,37 @@ static SlabTable make_table(void* const* slabs, int P) {
   return t;
 }
 
+// The part of a caller's split workspace that a launch of this attention shape uses: its
+// counters and partials (empty when the plan does not split or there is no workspace).
+static Range split_ws_range(const void* ws, unsigned long long ws_bytes, int B, int S, int H, int D) {
+  if (ws == nullptr) return Range{0, 0};
+  const unsigned long long used = attn_ws_used(B, S, H, D, ws_bytes);
+  return used ? range_of(ws, used) : Range{0, 0};
+}
+
+// Split workspace checks: 16-byte aligned, and the range the launch uses disjoint from every
+// range in `others` (the call's inputs, outputs and other buffers).
+static int check_split_ws(const void* ws, Range used, const Range* others, int n_others) {
+  if (ws == nullptr) return XSTAGE_OK;
+  if (!aligned16(ws)) return XSTAGE_ERR_INVALID;
+  for (int o = 0; o < n_others; ++o)
+    if (overlaps(used, others[o])) return XSTAGE_ERR_INVALID;
+  return XSTAGE_OK;
+}
+
 static int check_attn_slabs(const void* q, const void* k, const void* v, void* const* slabs, int B, int S, int H,
-                            int D, int P, float scale, const void* extra, unsigned long long extra_bytes) {
+                            int D, int P, float scale, const void* extra, unsigned long long extra_bytes,
+                            const void* ws, unsigned long long ws_bytes) {
   int st = check_shape(B, S, H, D, P);
   if (st != XSTAGE_OK) return st;
   st = check_qkv(q, k, v, scale);
   if (st != XSTAGE_OK) return st;
   const unsigned long long tb = tensor_bytes(B, S, H, D);
-  Range others[4] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(extra, extra_bytes)};
-  return check_slabs(slabs, P, tb / (unsigned long long)P, others, extra ? 4 : 3);
+  const Range wr = split_ws_range(ws, ws_bytes, B, S, H, D);
+  Range others[5] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(extra, extra_bytes), wr};
+  st = check_split_ws(ws, wr, others, 4);
+  if (st != XSTAGE_OK) return st;
+  return check_slabs(slabs, P, tb / (unsigned long long)P, others, 5);
 }
 }  // namespace xstage
 
@@ -44,20 +69,32 @@ using namespace xstage;
 
 extern "C" {
 
-int xstage_attn_a2a_fwd(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
-                        int H_local, int D, int P, float scale, void* stream) {
-  const int st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, nullptr, 0);
+int xstage_attn_split_ws_size(int B, int S, int H_local, int D, unsigned long long* bytes) {
+  if (bytes == nullptr) return XSTAGE_ERR_INVALID;
+  const int st = check_shape(B, S, H_local, D, 1);
   if (st != XSTAGE_OK) return st;
-  return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale,
+  *bytes = attn_ws_used(B, S, H_local, D, ~0ull);
+  return XSTAGE_OK;
+}
+
+int xstage_attn_a2a_fwd(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
+                        int H_local, int D, int P, float scale, void* split_ws, unsigned long long split_ws_bytes,
+                        void* stream) {
+  const int st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, nullptr, 0, split_ws,
+                                  split_ws_bytes);
+  if (st != XSTAGE_OK) return st;
+  return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale, split_ws, split_ws_bytes,
                          static_cast<hipStream_t>(stream));
 }
 
 int xstage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int S, int H_local, int D,
-                    float scale, void* stream) {
+                    float scale, void* split_ws, unsigned long long split_ws_bytes, void* stream) {
   void* slabs[1] = {out};
-  const int st = check_attn_slabs(q, k, v, out ? slabs : nullptr, B, S, H_local, D, 1, scale, nullptr, 0);
+  const int st = check_attn_slabs(q, k, v, out ? slabs : nullptr, B, S, H_local, D, 1, scale, nullptr, 0, split_ws,
+                                  split_ws_bytes);
   if (st != XSTAGE_OK) return st;
-  return launch_attn_any(q, k, v, make_table(slabs, 1), B, S, H_local, D, 1, scale, static_cast<hipStream_t>(stream));
+  return launch_attn_any(q, k, v, make_table(slabs, 1), B, S, H_local, D, 1, scale, split_ws, split_ws_bytes,
+                         static_cast<hipStream_t>(stream));
 }
 
 int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int H_local, int D, int P,
@@ -73,7 +110,8 @@ int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int
 }
 
 int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* workspace, void* const* out_slabs,
-                            int B, int S, int H_local, int D, int P, float scale, void* stream) {
+                            int B, int S, int H_local, int D, int P, float scale, void* split_ws,
+                            unsigned long long split_ws_bytes, void* stream) {
   int st = check_shape(B, S, H_local, D, P);
   if (st != XSTAGE_OK) return st;
   if (workspace == nullptr || !aligned16(workspace)) return XSTAGE_ERR_INVALID;
@@ -81,17 +119,18 @@ int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* w
   const Range ws = range_of(workspace, tb);
   if (q && (overlaps(ws, range_of(q, tb)) || overlaps(ws, range_of(k, tb)) || overlaps(ws, range_of(v, tb))))
     return XSTAGE_ERR_INVALID;
-  st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, workspace, tb);
+  st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, workspace, tb, split_ws, split_ws_bytes);
   if (st != XSTAGE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* one[1] = {workspace};
-  st = launch_attn_any(q, k, v, make_table(one, 1), B, S, H_local, D, 1, scale, s);
+  st = launch_attn_any(q, k, v, make_table(one, 1), B, S, H_local, D, 1, scale, split_ws, split_ws_bytes, s);
   if (st != XSTAGE_OK) return st;
   return launch_scatter(workspace, make_table(out_slabs, P), B, S, H_local, D, P, s);
 }
 
 int xstage_attn_a2a_fwd_strided(const void* q, const void* k, const void* v, void* const* out_dst, int B, int S,
-                                int H_local, int D, int P, int H_dst, int h_dst0, float scale, void* stream) {
+                                int H_local, int D, int P, int H_dst, int h_dst0, float scale, void* split_ws,
+                                unsigned long long split_ws_bytes, void* stream) {
   int st = check_shape(B, S, H_local, D, P);
   if (st != XSTAGE_OK) return st;
   if (H_dst < H_local || h_dst0 < 0 || h_dst0 > H_dst - H_local) return XSTAGE_ERR_INVALID;
@@ -100,26 +139,29 @@ int xstage_attn_a2a_fwd_strided(const void* q, const void* k, const void* v, voi
   st = check_qkv(q, k, v, scale);
   if (st != XSTAGE_OK) return st;
   const unsigned long long tb = tensor_bytes(B, S, H_local, D);
-  const Range others[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
-  st = check_slabs(out_dst, P, tensor_bytes(B, S, H_dst, D) / (unsigned long long)P, others, 3);
+  const Range wr = split_ws_range(split_ws, split_ws_bytes, B, S, H_local, D);
+  const Range others[4] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), wr};
+  st = check_split_ws(split_ws, wr, others, 3);
+  if (st != XSTAGE_OK) return st;
+  st = check_slabs(out_dst, P, tensor_bytes(B, S, H_dst, D) / (unsigned long long)P, others, 4);
   if (st != XSTAGE_OK) return st;
   Layout lay;
   lay.dst_heads = H_dst;
   lay.dst_head0 = h_dst0;
-  return launch_attn_any(q, k, v, make_table(out_dst, P), B, S, H_local, D, P, scale, static_cast<hipStream_t>(stream),
-                         0, nullptr, &lay);
+  return launch_attn_any(q, k, v, make_table(out_dst, P), B, S, H_local, D, P, scale, split_ws, split_ws_bytes,
+                         static_cast<hipStream_t>(stream), 0, nullptr, &lay);
 }
 
 int xstage_ulysses_attn_fwd(const void* const* q_src, const void* const* k_src, const void* const* v_src,
                             void* const* out_dst, int B, int S, int H, int H_local, int h0, int D, int P, float scale,
-                            void* stream) {
+                            void* split_ws, unsigned long long split_ws_bytes, void* stream) {
   int st = check_shape(B, S, H, D, P);
   if (st != XSTAGE_OK) return st;
   if (H_local <= 0 || H_local > H || h0 < 0 || h0 > H - H_local) return XSTAGE_ERR_INVALID;
   if (P > kMaxSrc) return XSTAGE_ERR_UNSUPPORTED;
   if (q_src == nullptr || k_src == nullptr || v_src == nullptr || !std::isfinite(scale)) return XSTAGE_ERR_INVALID;
   const unsigned long long shard = tensor_bytes(B, S, H, D) / (unsigned long long)P;
-  Range src_ranges[3 * kMaxSrc];
+  Range src_ranges[3 * kMaxSrc + 1];
   SrcTable t = {};
   for (int p = 0; p < P; ++p) {
     const void* ptrs[3] = {q_src[p], k_src[p], v_src[p]};
@@ -131,7 +173,11 @@ int xstage_ulysses_attn_fwd(const void* const* q_src, const void* const* k_src, 
     t.k[p] = static_cast<const uint16_t*>(k_src[p]);
     t.v[p] = static_cast<const uint16_t*>(v_src[p]);
   }
-  st = check_slabs(out_dst, P, shard, src_ranges, 3 * P);
+  const Range wr = split_ws_range(split_ws, split_ws_bytes, B, S, H_local, D);
+  st = check_split_ws(split_ws, wr, src_ranges, 3 * P);
+  if (st != XSTAGE_OK) return st;
+  src_ranges[3 * P] = wr;
+  st = check_slabs(out_dst, P, shard, src_ranges, 3 * P + 1);
   if (st != XSTAGE_OK) return st;
   Layout lay;
   lay.src = &t;
@@ -139,8 +185,8 @@ int xstage_ulysses_attn_fwd(const void* const* q_src, const void* const* k_src, 
   lay.src_head0 = h0;
   lay.dst_heads = H;
   lay.dst_head0 = h0;
-  return launch_attn_any(q_src[0], k_src[0], v_src[0], make_table(out_dst, P), B, S, H_local, D, P, scale,
-                         static_cast<hipStream_t>(stream), 0, nullptr, &lay);
+  return launch_attn_any(q_src[0], k_src[0], v_src[0], make_table(out_dst, P), B, S, H_local, D, P, scale, split_ws,
+                         split_ws_bytes, static_cast<hipStream_t>(stream), 0, nullptr, &lay);
 }
 
 // Shared checks of the Ulysses layouts: P shard pointers (non-null, aligned) of
@@ -193,7 +239,8 @@ int xstage_a2a_scatter_strided(const void* in, void* const* out_dst, int B, int 
 
 int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_src, const void* const* v_src,
                                 void* workspace, void* const* out_dst, int B, int S, int H, int H_local, int h0,
-                                int D, int P, float scale, void* stream) {
+                                int D, int P, float scale, void* split_ws, unsigned long long split_ws_bytes,
+                                void* stream) {
   int st = check_shape(B, S, H, D, P);
   if (st != XSTAGE_OK) return st;
   if (H_local <= 0 || H_local > H || h0 < 0 || h0 > H - H_local) return XSTAGE_ERR_INVALID;
@@ -209,6 +256,10 @@ int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_s
   if (!disjoint_from(ws, src)) return XSTAGE_ERR_INVALID;
   std::vector<Range> others = src;
   others.push_back(ws);
+  const Range wr = split_ws_range(split_ws, split_ws_bytes, B, S, H_local, D);
+  st = check_split_ws(split_ws, wr, others.data(), (int)others.size());
+  if (st != XSTAGE_OK) return st;
+  others.push_back(wr);
   st = check_slabs(out_dst, P, shard, others.data(), (int)others.size());
   if (st != XSTAGE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -223,7 +274,7 @@ int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_s
     st = launch_slice_copy(srcs, 1, H * D, h0 * D, dst, 0, H_local * D, 0, B, S, H_local, D, P, s);
     if (st != XSTAGE_OK) return st;
   }
-  st = launch_attn_any(qc[0], kc[0], vc[0], make_table(oc, 1), B, S, H_local, D, 1, scale, s);
+  st = launch_attn_any(qc[0], kc[0], vc[0], make_table(oc, 1), B, S, H_local, D, 1, scale, split_ws, split_ws_bytes, s);
   if (st != XSTAGE_OK) return st;
   const void* osrc[1] = {oc[0]};
   return launch_slice_copy(osrc, 0, H_local * D, 0, out_dst, 1, H * D, h0 * D, B, S, H_local, D, P, s);
@@ -231,7 +282,8 @@ int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_s
 
 int xstage_ulysses_attn_fwd_kv_staged(const void* const* q_src, const void* const* k_src, const void* const* v_src,
                                       void* workspace, void* const* out_dst, int B, int S, int H, int H_local, int h0,
-                                      int D, int P, float scale, void* stream) {
+                                      int D, int P, float scale, void* split_ws, unsigned long long split_ws_bytes,
+                                      void* stream) {
   int st = check_shape(B, S, H, D, P);
   if (st != XSTAGE_OK) return st;
   if (H_local <= 0 || H_local > H || h0 < 0 || h0 > H - H_local) return XSTAGE_ERR_INVALID;
@@ -248,6 +300,10 @@ int xstage_ulysses_attn_fwd_kv_staged(const void* const* q_src, const void* cons
   if (!disjoint_from(ws, src)) return XSTAGE_ERR_INVALID;
   std::vector<Range> others = src;
   others.push_back(ws);
+  const Range wr = split_ws_range(split_ws, split_ws_bytes, B, S, H_local, D);
+  st = check_split_ws(split_ws, wr, others.data(), (int)others.size());
+  if (st != XSTAGE_OK) return st;
+  others.push_back(wr);
   st = check_slabs(out_dst, P, shard, others.data(), (int)others.size());
   if (st != XSTAGE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -267,42 +323,45 @@ int xstage_ulysses_attn_fwd_kv_staged(const void* const* q_src, const void* cons
   lay.src_head0 = h0;
   lay.dst_heads = H;
   lay.dst_head0 = h0;
-  return launch_attn_any(q_src[0], kc[0], vc[0], make_table(out_dst, P), B, S, H_local, D, P, scale, s, 0, nullptr,
-                         &lay);
+  return launch_attn_any(q_src[0], kc[0], vc[0], make_table(out_dst, P), B, S, H_local, D, P, scale, split_ws,
+                         split_ws_bytes, s, 0, nullptr, &lay);
 }
 
-int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_split) {
+int xstage_attn_a2a_plan(int B, int S, int H_local, int D, unsigned long long split_ws_bytes, int* n_workgroups,
+                         int* n_split) {
   if (n_workgroups == nullptr) return XSTAGE_ERR_INVALID;
   const int st = check_shape(B, S, H_local, D, 1);
   if (st != XSTAGE_OK) return st;
-  *n_workgroups = attn_workgroups(B, S, H_local, D, n_split);
+  *n_workgroups = attn_workgroups(B, S, H_local, D, split_ws_bytes, n_split);
   return XSTAGE_OK;
 }
 
-int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, int cap, int* tile, int* split, int* j0, int* j1,
-                             int* n_workgroups) {
+int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, unsigned long long split_ws_bytes, int cap, int* tile,
+                             int* split, int* j0, int* j1, int* n_workgroups) {
   if (n_workgroups == nullptr || cap < 0 || (cap > 0 && (!tile || !split || !j0 || !j1))) return XSTAGE_ERR_INVALID;
   const int st = check_shape(B, S, H_local, D, 1);
   if (st != XSTAGE_OK) return st;
-  *n_workgroups = attn_schedule(B, S, H_local, D, cap, tile, split, j0, j1);
+  *n_workgroups = attn_schedule(B, S, H_local, D, split_ws_bytes, cap, tile, split, j0, j1);
   return *n_workgroups > cap ? XSTAGE_ERR_INVALID : XSTAGE_OK;
 }
 
 int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
                                int H_local, int D, int P, float scale, int mode, unsigned long long* stamps,
-                               void* stream) {
+                               void* split_ws, unsigned long long split_ws_bytes, void* stream) {
   if (mode < 0 || mode > 3 || stamps == nullptr || (reinterpret_cast<uintptr_t>(stamps) & 7u) != 0)
     return XSTAGE_ERR_INVALID;
   int st = check_shape(B, S, H_local, D, P);
   if (st != XSTAGE_OK) return st;
-  const unsigned long long stamp_bytes = (unsigned long long)attn_workgroups(B, S, H_local, D, nullptr) * 16ull * 8ull;
+  const unsigned long long stamp_bytes =
+      (unsigned long long)attn_workgroups(B, S, H_local, D, split_ws ? split_ws_bytes : 0ull, nullptr) * 16ull * 8ull;
   const Range sr = range_of(stamps, stamp_bytes);
   const unsigned long long tb = tensor_bytes(B, S, H_local, D);
   if (q && (overlaps(sr, range_of(q, tb)) || overlaps(sr, range_of(k, tb)) || overlaps(sr, range_of(v, tb))))
     return XSTAGE_ERR_INVALID;
-  st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, stamps, stamp_bytes);
+  st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, stamps, stamp_bytes, split_ws,
+                        split_ws_bytes);
   if (st != XSTAGE_OK) return st;
-  return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale,
+  return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale, split_ws, split_ws_bytes,
                          static_cast<hipStream_t>(stream), 1 + mode, stamps);
 }
 

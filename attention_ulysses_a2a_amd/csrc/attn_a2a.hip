@@ -74,7 +74,8 @@ struct AttnArgs {
   int dst_hs, dst_h0;
   float c;           // |scale| * log2(e): scores are turned into base-2 logits
   uint32_t qflip;    // 0x80008000 for a negative scale: Q is negated on load
-  f32x4* partial;    // split partials: [tile][split][wave][chunk][64 lanes] (n_split > 1)
+  void* partial;      // split partials: [tile][split][wave][chunk][64 lanes] (n_split > 1)
+  int partial_bytes;  // bytes of the partial area (< 2^31)
   uint32_t* counters;  // per-tile arrival counters, zero between launches (n_split > 1)
   unsigned long long* stamps;  // traced modes: [workgroup][wave][4] wall-clock ticks
   int clock_stamps;  // traced modes: entries 2, 3 hold shader-clock ticks at start / loop end
@@ -518,10 +519,18 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
     // in the last place relative to each partial, inside the output's own rounding scale.
     constexpr int OCH = 2 * C::DT;
     constexpr int PREC = OCH + 1;
-    auto rec = [&](int sp) { return a.partial + ((size_t)(tile * a.n_split + sp) * 4 + w) * PREC * 64 + lane; };
+    // The workspace is ordinary device memory, cached in each XCD's own L2, and the splits of a
+    // tile may run on different XCDs.  Every access to a record therefore has device scope
+    // (sc1): stores write through the local L2 to the device's coherence point, loads are
+    // served from there, never from a stale local line.  Ordering (see the arrival below):
+    // a wave's record stores complete before the barrier, the barrier before the arrival
+    // count, the count before the last arriver's loads; no cache write-back or invalidate.
+    constexpr int kDeviceScope = 16;  // cache policy bits: sc1
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(a.partial, (short)0, a.partial_bytes, 0x00020000);
+    auto rec = [&](int sp) { return (((uint32_t)(tile * a.n_split + sp) * 4u + (uint32_t)w) * PREC * 64u + (uint32_t)lane) * 16u; };
     u32x4 own[OCH];  // this split's record, kept for the merge should it arrive last
     {
-      f32x4* r = rec(split);
+      const uint32_t r = rec(split);
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -530,16 +539,15 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
           const int e0 = 8 * hh;
           own[2 * dt + hh] = u32x4{pack_bf16x2(x[e0 + 0], x[e0 + 1]), pack_bf16x2(x[e0 + 2], x[e0 + 3]),
                                    pack_bf16x2(x[e0 + 4], x[e0 + 5]), pack_bf16x2(x[e0 + 6], x[e0 + 7])};
-          reinterpret_cast<u32x4*>(r)[(2 * dt + hh) * 64] = own[2 * dt + hh];
+          __builtin_amdgcn_raw_buffer_store_b128(own[2 * dt + hh], prs, r + (2 * dt + hh) * 1024u, 0, kDeviceScope);
         }
-      r[OCH * 64] = f32x4{m_run, l_run, 0.f, 0.f};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m_run, l_run, 0.f, 0.f}), prs,
+                                             r + OCH * 1024u, 0, kDeviceScope);
     }
     const f32x4 own_ml = {m_run, l_run, 0.f, 0.f};
-    // The partials and counters are in uncached memory: once this wave's stores have
-    // completed they are visible device-wide, and the counter is updated at memory.  A
-    // workgroup-scope release (wait for the stores) and the barrier order them before the
-    // arrival count; the reads below bypass every cache.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    // Wait until this wave's record stores have completed (device-scope stores complete once
+    // they reach the coherence point); the barrier then orders all four waves' records before
+    // the arrival count, an agent-scope atomic performed at the coherence point.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
@@ -550,10 +558,12 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
     }
     __syncthreads();
     if (!last_flag) return;
+    // The last arriver saw every other split's count, each issued after that split's records
+    // had completed; its device-scope loads, issued after the count returned, read them.
     // Merge in split order (own partial included, as the bits of its record), so the result
-    // does not depend on which split arrived last.  Uncached reads have a long latency: the
-    // records of NB splits are requested together and folded in with a running-max rescale,
-    // so that up to NB splits cost one round trip.
+    // does not depend on which split arrived last.  The records of NB splits are requested
+    // together and folded in with a running-max rescale, so that up to NB splits cost one
+    // round trip to the coherence point.
     constexpr int NB = 4;
     float m_acc = -INFINITY, l_acc = 0.f;
 #pragma unroll
@@ -568,10 +578,10 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
 #pragma unroll
           for (int ch = 0; ch < OCH; ++ch) ob[i][ch] = own[ch];
         } else if (s0 + i < a.n_split) {
-          const f32x4* r = rec(s0 + i);
-          ml[i] = r[OCH * 64];
+          const uint32_t r = rec(s0 + i);
+          ml[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, r + OCH * 1024u, 0, kDeviceScope));
 #pragma unroll
-          for (int ch = 0; ch < OCH; ++ch) ob[i][ch] = reinterpret_cast<const u32x4*>(r)[ch * 64];
+          for (int ch = 0; ch < OCH; ++ch) ob[i][ch] = __builtin_amdgcn_raw_buffer_load_b128(prs, r + ch * 1024u, 0, kDeviceScope);
         } else {
           ml[i] = f32x4{-INFINITY, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -709,7 +719,8 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.n_units = B * H * a.n_mtiles * plan.n_split;
   a.c = fabsf(scale) * kLog2e;
   a.qflip = std::signbit(scale) ? 0x80008000u : 0u;
-  a.partial = static_cast<f32x4*>(plan.partial);
+  a.partial = plan.partial;
+  a.partial_bytes = (int)((size_t)a.n_units * partial_bytes_per_unit(D));
   a.counters = plan.counters;
   a.stamps = stamps;
   a.clock_stamps = mode == kTracedClock;
@@ -742,21 +753,29 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
 }
 
-// Bytes of split partials for one tile and one split: 4 waves x (2 bf16 O chunks per 32-wide
-// d tile + one (m, l) chunk) x 64 lanes x 16 B.
-static size_t partial_bytes_per_unit(int D) { return (size_t)4 * (2 * (D / 32) + 1) * 64 * 16; }
-
-int attn_workgroups(int B, int S, int H, int D, int* n_split) {
+int attn_workgroups(int B, int S, int H, int D, unsigned long long ws_bytes, int* n_split) {
   const int n_tiles = B * H * ((S + 127) / 128);
-  const SplitPlan plan = choose_split(n_tiles, (S + 63) / 64, D, partial_bytes_per_unit(D));
+  size_t used = 0;
+  const SplitPlan plan = plan_with_workspace(n_tiles, (S + 63) / 64, D, ws_bytes, &used);
   if (n_split) *n_split = plan.n_split;
   return n_tiles * plan.n_split;
 }
 
-int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, int* j0, int* j1) {
+// Workspace bytes a launch of this shape uses given ws_bytes of workspace (0: no split);
+// ws_bytes = ~0 gives the bytes of the unconstrained plan.
+unsigned long long attn_ws_used(int B, int S, int H, int D, unsigned long long ws_bytes) {
+  const int n_tiles = B * H * ((S + 127) / 128);
+  size_t used = 0;
+  plan_with_workspace(n_tiles, (S + 63) / 64, D, ws_bytes, &used);
+  return used;
+}
+
+int attn_schedule(int B, int S, int H, int D, unsigned long long ws_bytes, int cap, int* tile, int* split, int* j0,
+                  int* j1) {
   const int n_tiles = B * H * ((S + 127) / 128);
   const int nkv = (S + 63) / 64;
-  const SplitPlan plan = choose_split(n_tiles, nkv, D, partial_bytes_per_unit(D));
+  size_t used = 0;
+  const SplitPlan plan = plan_with_workspace(n_tiles, nkv, D, ws_bytes, &used);
   const int n = n_tiles * plan.n_split;
   if (n > cap) return n;
   const UnitTable* tab = plan.n_split > 1 ? unit_table(n_tiles, nkv, plan.n_split) : nullptr;
@@ -780,16 +799,17 @@ int attn_schedule(int B, int S, int H, int D, int cap, int* tile, int* split, in
 }
 
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
-                    int P, float scale, hipStream_t stream, int mode, unsigned long long* stamps, const Layout* layout) {
+                    int P, float scale, void* ws, unsigned long long ws_bytes, hipStream_t stream, int mode,
+                    unsigned long long* stamps, const Layout* layout) {
   static const Layout kDefaultLayout;
   const Layout& lay = layout ? *layout : kDefaultLayout;
   const int n_tiles = B * H * ((S + 127) / 128);
   const int nkv = (S + 63) / 64;
-  SplitPlan plan = choose_split(n_tiles, nkv, D, partial_bytes_per_unit(D));
+  size_t used = 0;
+  SplitPlan plan = plan_with_workspace(n_tiles, nkv, D, ws ? ws_bytes : 0ull, &used);
   if (plan.n_split > 1) {
-    const int st = acquire_workspace(stream, (size_t)n_tiles * plan.n_split * partial_bytes_per_unit(D), n_tiles,
-                                     &plan.partial, &plan.counters);
-    if (st != XSTAGE_OK) return st;
+    plan.counters = static_cast<uint32_t*>(ws);
+    plan.partial = static_cast<char*>(ws) + kCounterAreaBytes;
   }
   if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, stream);
   return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, stream);

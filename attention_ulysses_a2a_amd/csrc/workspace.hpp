@@ -1,5 +1,6 @@
-// Host side of the key-range split: how many splits a launch uses, and the library-owned
-// buffers (split partials, per-tile arrival counters) that the splits merge through.
+// Host side of the key-range split: how many splits a launch uses, and the layout of the
+// caller-owned split workspace (per-tile arrival counters, then the split partials) that
+// the splits merge through.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,10 +16,31 @@ struct SplitPlan {
   uint32_t* counters = nullptr;  // n_tiles arrival counters, zero between launches
 };
 
+// Largest split-partial area a plan may use (the workspace size query reports plans up to
+// this; a launch given less workspace splits less).
+constexpr size_t kSplitPartialCap = size_t(128) << 20;
+
+// Bytes of split partials of one (tile, split) unit: 4 waves x (2 bf16 O chunks per 32-wide
+// d tile + one (m, l) chunk) x 64 lanes x 16 B.
+inline size_t partial_bytes_per_unit(int D) { return (size_t)4 * (2 * (D / 32) + 1) * 64 * 16; }
+
+// Workspace layout, the same for every shape: kSplitMaxTiles uint32 arrival counters (tile t
+// uses counter t), then the partials.  The counters of any later call, whatever its shape,
+// therefore never overlap an earlier call's partials, and every call leaves them at zero.
+// Shapes with more tiles are not split (they fill the device without it).
+constexpr int kSplitMaxTiles = 4096;
+constexpr size_t kCounterAreaBytes = (size_t)kSplitMaxTiles * 4;
+
 // Picks the key-split count of `n_tiles` tiles of 128 query rows over `nkv` blocks of 64
 // keys (head dimension D) on the current device, from a cost model of rounds of
-// co-resident workgroups (two per compute unit) and of the merge of split tiles.
-SplitPlan choose_split(int n_tiles, int nkv, int D, size_t partial_bytes_per_unit);
+// co-resident workgroups (two per compute unit) and of the merge of split tiles, among the
+// plans whose partials fit `partial_capacity` bytes (0: no split).
+SplitPlan choose_split(int n_tiles, int nkv, int D, size_t partial_capacity);
+
+// Plan of a launch given `ws_bytes` of split workspace (ws_bytes = 0: no workspace): the
+// counters take kCounterAreaBytes, the partials at most the rest (and at most
+// kSplitPartialCap); more than kSplitMaxTiles tiles are never split.  Returns the workspace bytes the plan uses in *used (0 without split).
+SplitPlan plan_with_workspace(int n_tiles, int nkv, int D, unsigned long long ws_bytes, size_t* used);
 
 // Per-workgroup work of a launch whose workgroups all fit on the device at once.  Workgroups
 // are dispatched in index order, round-robin over the 8 XCDs (i % 8), and each XCD fills
@@ -49,10 +71,5 @@ bool build_unit_table(int n_tiles, int nkv, int n_split, int cus, UnitTable* tab
 // Cached build_unit_table for the current device (nullptr when out of scope).
 const UnitTable* unit_table(int n_tiles, int nkv, int n_split);
 
-// Returns buffers of at least `partial_bytes` and `n_counters` zeroed counters owned by the
-// library for (current device, stream).  Grows them on demand: growing synchronizes
-// `stream` first (the old buffers may still be read by earlier launches on it).
-int acquire_workspace(hipStream_t stream, size_t partial_bytes, int n_counters, void** partial,
-                      uint32_t** counters);
 
 }  // namespace xstage

@@ -92,13 +92,14 @@ def run_study(torch, xs, S_list=DEFAULT_S, H=3, D=128, P=8, seed=11, target_s=0.
         out1 = torch.empty((1, S, H, D), dtype=torch.bfloat16, device="cuda")
         nwg, nsp = xs.xstage_attn_a2a_plan(1, S, H, D)
         stamps = [torch.zeros(nwg * 16, dtype=torch.int64, device="cuda") for _ in range(4)]
+        sws = xs.split_workspace(1, S, H, D)
         calls = {
-            "attn": xs.bind("xstage_attn_fwd", q, k, v, out1, w.scale),
-            "fused": xs.bind("xstage_attn_a2a_fwd", q, k, v, sl, w.scale),
-            "traced": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 0, stamps[0], w.scale),
-            "coupled": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 1, stamps[1], w.scale),
-            "nostore": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 2, stamps[2], w.scale),
-            "clock": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 3, stamps[3], w.scale),
+            "attn": xs.bind("xstage_attn_fwd", q, k, v, out1, w.scale, split_ws=sws),
+            "fused": xs.bind("xstage_attn_a2a_fwd", q, k, v, sl, w.scale, split_ws=sws),
+            "traced": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 0, stamps[0], w.scale, split_ws=sws),
+            "coupled": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 1, stamps[1], w.scale, split_ws=sws),
+            "nostore": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 2, stamps[2], w.scale, split_ws=sws),
+            "clock": xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, sl, 3, stamps[3], w.scale, split_ws=sws),
         }
         t_est = _time(torch, calls["fused"], 3, 3)
         n = max(20, min(2000, int(target_s / max(t_est, 1e-6))))
@@ -125,6 +126,6 @@ def run_study(torch, xs, S_list=DEFAULT_S, H=3, D=128, P=8, seed=11, target_s=0.
         }
         rows.append(row)
         emit(json.dumps(row))
-        del q, k, v, slabs, out1, stamps, calls
+        del q, k, v, slabs, out1, stamps, calls, sws
         torch.cuda.empty_cache()
     return rows

@@ -6,11 +6,17 @@ H_local=3, D=128, P=8 destination slabs of [576, 3, 128]): non-causal attention 
 sequence with the post-attention all-to-all written from the epilogue.  Inputs are seeded
 synthetic bf16 tensors resident in HBM before the timed region.  Prints one JSON line.
 
-Extra legs (reported inside the same line): the serial path (attention into a contiguous
-buffer, then the separate scatter kernel), attention alone (P=1), the full-head Ulysses
-layouts (strided destination; the whole layer reading its inputs from P sequence shards),
-and the CPU oracle timed on a bounded sample of the same workload (``cpu_baseline``).  ``--bg`` instead runs the
-Burst-Gap store sweep and prints one JSON line per point plus the fitted parameters.
+Every leg runs after one common settle phase (``--settle-s`` seconds of fused launches: the
+first launches of a process run up to ~6 % slow while the chip ramps up), then each leg gets
+the same ``--warmup`` untimed and ``--steps`` timed launches.  The headline is one block of
+exactly ``--steps`` fused launches between two synchronisations, timed with HIP events on the
+stream the kernel runs on.  Extra legs (reported inside the same line; the ratios come from
+three interleaved rounds of every leg): the serial path (attention into a contiguous buffer,
+then the separate scatter kernel), attention alone (P=1), the full-head Ulysses layouts
+(strided destination; the whole layer reading its inputs from P sequence shards), and the
+CPU oracle timed on a bounded sample of the same workload (``cpu_baseline``).  ``--bg``
+instead runs the Burst-Gap store sweep and prints one JSON line per point plus the fitted
+parameters; ``--cpu-oracle-configs`` times the oracle on every configuration.
 """
 
 from __future__ import annotations
@@ -48,6 +54,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of fused launches before any leg (chip ramp-up; see the module docstring)")
+    ap.add_argument("--cpu-oracle-configs", action="store_true",
+                    help="time the float64 oracle on every workload in full (plus tiny on one core)")
     ap.add_argument("--workload", default="flux1024", help="synth workload name (tiny, flux1024, flux2048, video)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -77,17 +87,32 @@ def timed(fn, steps, warmup, torch):
     return start.elapsed_time(end) / steps
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, qb, kb, vb, seconds):
     """Times the oracle (as it stands) on whole query-row blocks of the workload."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads = blas_threads()
     q, k, v = (oracle.bf16_bits_to_f64(x) for x in (qb, kb, vb))
     rows_done = 0
     t0 = time.perf_counter()
@@ -109,7 +134,45 @@ def cpu_baseline(w, qb, kb, vb, seconds):
         "sample": f"{rows_done} query rows x all {w.H} heads (blocks of {block}) of the {w.name} workload over the "
                   f"full key set, float64 numpy, {dt:.1f} s",
         "seconds": dt,
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_oracle_configs():
+    """The float64 oracle (as it stands) on every workload in full, on this host's cores, and the
+    tiny workload also on one core: one JSON line per run."""
+    import numpy as np
+
+    import oracle
+    from synth import make_inputs, workload
+
+    def run(name):
+        w = workload(name)
+        q, k, v = (oracle.bf16_bits_to_f64(x) for x in make_inputs(w))
+        t0 = time.perf_counter()
+        o = oracle.attention_fp64(q, k, v, w.scale)
+        oracle.ulysses_scatter(o, w.P)
+        dt = time.perf_counter() - t0
+        return w, dt
+
+    from threadpoolctl import threadpool_limits
+
+    lines = []
+    for name, one_core in (("tiny", True), ("tiny", False), ("flux1024", False), ("flux2048", False),
+                           ("video", False)):
+        if one_core:
+            with threadpool_limits(limits=1):
+                w, dt = run(name)
+                threads = 1
+        else:
+            w, dt = run(name)
+            threads = blas_threads()
+        rec = {"cpu_oracle": name, "B": w.B, "S": w.S, "H_local": w.H, "D": w.D, "P": w.P,
+               "seconds": round(dt, 4), "GFLOPs": round(w.flops / dt / 1e9, 2), "threads": threads,
+               "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
+        print(json.dumps(rec), flush=True)
+        lines.append(rec)
+    return lines
 
 
 def traffic_entry(achieved_bytes_per_launch=None):
@@ -140,12 +203,22 @@ def bench_attention(args, torch, xs):
     out1 = torch.empty((w.B, w.S, w.H, w.D), dtype=torch.bfloat16, device="cuda")
     slab_list = [slabs[p] for p in range(w.P)]
 
+    # The caller-owned split workspace (zero-filled once; every call leaves it reusable).
+    sws = xs.split_workspace(w.B, w.S, w.H, w.D)
     # Prepared launches (arguments validated and marshalled once): the host issues each
     # step in a few microseconds, well under the kernel time, so the GPU never waits on it.
-    fused = xs.bind("xstage_attn_a2a_fwd", q, k, v, slab_list, w.scale)
-    unfused = xs.bind("xstage_attn_a2a_unfused", q, k, v, ws, slab_list, w.scale)
-    attn_only = xs.bind("xstage_attn_fwd", q, k, v, out1, w.scale)
+    fused = xs.bind("xstage_attn_a2a_fwd", q, k, v, slab_list, w.scale, split_ws=sws)
+    unfused = xs.bind("xstage_attn_a2a_unfused", q, k, v, ws, slab_list, w.scale, split_ws=sws)
+    attn_only = xs.bind("xstage_attn_fwd", q, k, v, out1, w.scale, split_ws=sws)
     scatter_only = xs.bind("xstage_a2a_scatter", ws, slab_list)
+
+    # settle: the first launches of a process run slow while the chip ramps up
+    settle_n, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(50):
+            fused()
+        settle_n += 50
+        torch.cuda.synchronize()
 
     # the timed region: exactly `steps` fused steps bracketed by synchronizations
     for _ in range(args.warmup):
@@ -161,12 +234,18 @@ def bench_attention(args, torch, xs):
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / args.steps
 
-    # comparison legs (outside the timed region); the first few hundred calls of a newly
-    # used path run slow on a fresh process, so each leg warms up with >= 300 calls
-    leg_warmup = max(args.warmup, 300)
-    ms_unfused = timed(unfused, args.steps, leg_warmup, torch)
-    ms_attn = timed(attn_only, args.steps, leg_warmup, torch)
-    ms_scatter = timed(scatter_only, args.steps, leg_warmup, torch)
+    # comparison legs: three interleaved rounds, every leg with the headline's warm-up and
+    # step count; the ratios are taken from the medians
+    import statistics
+
+    legs = {"fused": fused, "unfused": unfused, "attn": attn_only, "scatter": scatter_only}
+    per = {n: [] for n in legs}
+    for _ in range(3):
+        for n, fn in legs.items():
+            per[n].append(timed(fn, args.steps, args.warmup, torch))
+    med = {n: statistics.median(v) for n, v in per.items()}
+    ms_unfused, ms_attn, ms_scatter = med["unfused"], med["attn"], med["scatter"]
+    leg_warmup = args.warmup
 
     # Full-head Ulysses layouts, as rank 5 of a group of P ranks over H_local * P heads:
     # the strided epilogue (receive buffers [B, S/P, H, D], this rank's head columns) and the
@@ -177,15 +256,15 @@ def bench_attention(args, torch, xs):
     gen = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
     shards = [[torch.randn((w.B, w.S // w.P, H_all, w.D), generator=gen, device="cuda").to(torch.bfloat16)
                for _ in range(w.P)] for _ in range(3)]
-    strided = xs.bind("xstage_attn_a2a_fwd_strided", q, k, v, recv, h0, w.scale)
-    layer = xs.bind("xstage_ulysses_attn_fwd", shards[0], shards[1], shards[2], recv, w.H, h0, w.scale)
+    strided = xs.bind("xstage_attn_a2a_fwd_strided", q, k, v, recv, h0, w.scale, split_ws=sws)
+    layer = xs.bind("xstage_ulysses_attn_fwd", shards[0], shards[1], shards[2], recv, w.H, h0, w.scale, split_ws=sws)
     ws4 = torch.empty((4, w.B, w.S, w.H, w.D), dtype=torch.bfloat16, device="cuda")
     layer_serial = xs.bind("xstage_ulysses_attn_unfused", shards[0], shards[1], shards[2], ws4, recv, w.H, h0,
-                           w.scale)
+                           w.scale, split_ws=sws)
     ms_strided = timed(strided, args.steps, leg_warmup, torch)
     ms_layer = timed(layer, args.steps, leg_warmup, torch)
     layer_staged = xs.bind("xstage_ulysses_attn_fwd_kv_staged", shards[0], shards[1], shards[2], ws4[:2], recv,
-                           w.H, h0, w.scale)
+                           w.H, h0, w.scale, split_ws=sws)
     ms_layer_serial = timed(layer_serial, args.steps, leg_warmup, torch)
     ms_layer_staged = timed(layer_staged, args.steps, leg_warmup, torch)
     del shards, recv, ws4
@@ -195,7 +274,7 @@ def bench_attention(args, torch, xs):
     # peak assumes 2.4 GHz, while a chip running dense MFMA work clocks lower.
     nwg, _ = xs.xstage_attn_a2a_plan(w.B, w.S, w.H, w.D)
     stamps = torch.zeros(nwg * 16, dtype=torch.int64, device="cuda")
-    clocked = xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, slab_list, 3, stamps, w.scale)
+    clocked = xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, slab_list, 3, stamps, w.scale, split_ws=sws)
     for _ in range(args.warmup):
         fused()
     clocked()
@@ -227,8 +306,12 @@ def bench_attention(args, torch, xs):
             "parallelism": f"one GPU's Ulysses share (P={w.P} destination slabs in local HBM)",
         },
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "fused_vs_unfused": round(ms_unfused / ms, 4),
-        "fused_vs_attention_only": round(ms / ms_attn, 4),
+        "settle_s": round(args.settle_s, 3),
+        "settle_launches": settle_n,
+        "split_ws_bytes": 0 if sws is None else int(sws.numel()),
+        "fused_vs_unfused": round(ms_unfused / med["fused"], 4),
+        "fused_vs_attention_only": round(med["fused"] / ms_attn, 4),
+        "ms_fused_interleaved": med["fused"],
         "ms_unfused": ms_unfused,
         "ms_attention_only": ms_attn,
         "ms_scatter_only": ms_scatter,
@@ -326,6 +409,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     xs.lib()  # fail loudly if the HIP library is missing
+    if args.cpu_oracle_configs:
+        cpu_oracle_configs()
+        return
     if args.bg:
         from attention_ulysses_a2a_amd.bg_sweep import run_sweep
 
@@ -348,7 +434,8 @@ def main():
         q, k, v = (torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).cuda().view(torch.bfloat16)
                    for b in make_inputs(w))
         slabs = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device="cuda")
-        fused = xs.bind("xstage_attn_a2a_fwd", q, k, v, [slabs[p] for p in range(w.P)], w.scale)
+        sws = xs.split_workspace(w.B, w.S, w.H, w.D)
+        fused = xs.bind("xstage_attn_a2a_fwd", q, k, v, [slabs[p] for p in range(w.P)], w.scale, split_ws=sws)
         for _ in range(args.profile_launches):
             fused()
         torch.cuda.synchronize()

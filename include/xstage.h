@@ -27,23 +27,30 @@
  *   - `out_slabs` is a HOST array of P device pointers; the pointers are copied by value
  *     into the kernel arguments, so the array may be freed as soon as the call returns.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work and return;
- *     they never synchronize.  Except where stated, they never allocate or free memory.
- *   - Workspace (attention entry points): when a shape is split along the keys across
- *     workgroups (small B*H*S), the first such call on a (device, stream) allocates one
- *     library-owned uncached workspace (320 MiB of partial results, 4 MiB of counters,
- *     zeroed with one device synchronization) that lives until the process ends; later calls
- *     on that (device, stream) reuse it and allocate nothing.  Calls on one stream are
- *     ordered, so they never share it concurrently; calls on different streams use
- *     different workspaces.  A shape is split only as far as its partials fit the
- *     workspace; a failed allocation returns XSTAGE_ERR_HIP before any launch.
+ *     they never synchronize, never allocate and never free memory: the caller owns every
+ *     buffer.
+ *   - Split workspace (attention entry points: split_ws, split_ws_bytes).  When a shape has
+ *     few 128-row query tiles for the device (small B*H_local*S), the keys of each tile are
+ *     split over several workgroups whose partial results meet in a caller-owned workspace:
+ *     16 KiB of per-tile arrival counters, then the partials (the same layout for every
+ *     shape).  xstage_attn_split_ws_size gives the bytes the fastest plan uses (0 when the
+ *     shape is not split; at most 16 KiB + 128 MiB).  The split count is limited to what fits
+ *     in split_ws_bytes: a smaller workspace gives the same result up to fp32 summation
+ *     order, possibly more slowly, and split_ws = NULL runs without splits.  The workspace
+ *     is plain device memory (any allocator), 16-byte aligned, disjoint from every other
+ *     buffer of the call; it must hold zeros before its first use, and every call leaves
+ *     the counters it used at zero once it completes, so one workspace serves any later
+ *     call and shape.  Calls that may run concurrently (different streams) need separate
+ *     workspaces.
  *   - Errors: every argument check runs before any HIP call; on an error nothing is
  *     launched and no output byte is touched.  Faults inside kernels surface at the
  *     caller's next synchronization.  XSTAGE_ERR_HIP reports the HIP launch status.
  *   - Attention: O = softmax(scale * Q K^T) V per (b, h), non-causal, products and sums in
  *     fp32, output rounded to bf16 (round to nearest, ties to even).  scale may be any
  *     finite value, including 0 and negative values.
- *   - Thread safety: the only mutable state is the per-(device, stream) workspace table,
- *     guarded by a mutex; entry points may be called concurrently.
+ *   - Thread safety: the library keeps no device state; its host-side caches (CU count and
+ *     per-shape schedule tables) are guarded by a mutex; entry points may be called
+ *     concurrently.
  */
 #ifndef XSTAGE_H_
 #define XSTAGE_H_
@@ -71,12 +78,18 @@ typedef enum {
  * into the slab that owns its rows; the issuing wave does not wait for the stores and
  * goes on with its next tile.  Slabs must not overlap each other or q, k, v. */
 int xstage_attn_a2a_fwd(const void* q, const void* k, const void* v, void* const* out_slabs,
-                        int B, int S, int H_local, int D, int P, float scale, void* stream);
+                        int B, int S, int H_local, int D, int P, float scale, void* split_ws,
+                        unsigned long long split_ws_bytes, void* stream);
+
+/* Bytes of split workspace the attention entry points use for this shape at full speed
+ * (see the split workspace convention above); 0 when the shape is not split.  Host only. */
+int xstage_attn_split_ws_size(int B, int S, int H_local, int D, unsigned long long* bytes);
 
 /* Attention alone into a contiguous [B, S, H_local, D] output (the first half of the serial
  * baseline of "Results", FlashAttention-A2A).  `out` must not overlap q, k, v. */
 int xstage_attn_fwd(const void* q, const void* k, const void* v, void* out,
-                    int B, int S, int H_local, int D, float scale, void* stream);
+                    int B, int S, int H_local, int D, float scale, void* split_ws,
+                    unsigned long long split_ws_bytes, void* stream);
 
 /* xstage_attn_a2a_fwd with full-head destination buffers ("Contributions",
  * FlashAttention-A2A item: each output tile is stored straight into its destination's
@@ -90,7 +103,8 @@ int xstage_attn_fwd(const void* q, const void* k, const void* v, void* out,
  * each other or q, k, v.  With H_dst = H_local and h_dst0 = 0 this is xstage_attn_a2a_fwd. */
 int xstage_attn_a2a_fwd_strided(const void* q, const void* k, const void* v, void* const* out_dst,
                                 int B, int S, int H_local, int D, int P, int H_dst, int h_dst0,
-                                float scale, void* stream);
+                                float scale, void* split_ws, unsigned long long split_ws_bytes,
+                                void* stream);
 
 /* One rank's Ulysses attention layer with both all-to-alls fused into the attention kernel
  * (the post-attention one in the epilogue as in xstage_attn_a2a_fwd_strided, the
@@ -110,7 +124,8 @@ int xstage_attn_a2a_fwd_strided(const void* q, const void* k, const void* v, voi
  * calling xstage_attn_a2a_fwd_strided with H_dst = H, h_dst0 = h0, bit for bit. */
 int xstage_ulysses_attn_fwd(const void* const* q_src, const void* const* k_src,
                             const void* const* v_src, void* const* out_dst, int B, int S, int H,
-                            int H_local, int h0, int D, int P, float scale, void* stream);
+                            int H_local, int h0, int D, int P, float scale, void* split_ws,
+                            unsigned long long split_ws_bytes, void* stream);
 
 /* The pre-attention all-to-all of a Ulysses layer as a separate step (serial layer): copies
  * heads [h0, h0 + H_local) of the P sequence shards src_shards[p] ([B, S/P, H, D], HOST
@@ -136,7 +151,7 @@ int xstage_a2a_scatter_strided(const void* in, void* const* out_dst, int B, int 
 int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_src,
                                 const void* const* v_src, void* workspace, void* const* out_dst,
                                 int B, int S, int H, int H_local, int h0, int D, int P, float scale,
-                                void* stream);
+                                void* split_ws, unsigned long long split_ws_bytes, void* stream);
 
 /* Ulysses layer with K and V staged: xstage_ulysses_gather of k and v into the workspace,
  * then one attention launch that reads Q from the shards in place and writes its output
@@ -152,7 +167,8 @@ int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_s
 int xstage_ulysses_attn_fwd_kv_staged(const void* const* q_src, const void* const* k_src,
                                       const void* const* v_src, void* workspace,
                                       void* const* out_dst, int B, int S, int H, int H_local,
-                                      int h0, int D, int P, float scale, void* stream);
+                                      int h0, int D, int P, float scale, void* split_ws,
+                                      unsigned long long split_ws_bytes, void* stream);
 
 /* The separate all-to-all send step of the serial baseline: copies a contiguous
  * [B, S, H_local, D] tensor into the P slabs.  Slabs must not overlap `in` or each other. */
@@ -164,16 +180,20 @@ int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int
  * xstage_attn_a2a_fwd, bit for bit. */
 int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* workspace,
                             void* const* out_slabs, int B, int S, int H_local, int D, int P,
-                            float scale, void* stream);
+                            float scale, void* split_ws, unsigned long long split_ws_bytes,
+                            void* stream);
 
-/* Work decomposition of the attention entry points for this shape on the current device:
- * *n_workgroups workgroups of 4 waves (n_tiles x key splits, n_tiles = B * H_local *
- * ceil(S / 128)), *n_split key splits per 128-row tile (n_split may be NULL).  Host only;
- * sizes the stamps of xstage_attn_a2a_fwd_traced. */
-int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_split);
+/* Work decomposition of the attention entry points for this shape on the current device,
+ * given split_ws_bytes of split workspace (0: none): *n_workgroups workgroups of 4 waves
+ * (n_tiles x key splits, n_tiles = B * H_local * ceil(S / 128)), *n_split key splits per
+ * 128-row tile (n_split may be NULL).  Host only; sizes the stamps of
+ * xstage_attn_a2a_fwd_traced. */
+int xstage_attn_a2a_plan(int B, int S, int H_local, int D, unsigned long long split_ws_bytes,
+                         int* n_workgroups, int* n_split);
 
 /* The work decomposition xstage_attn_a2a_fwd uses for this shape on the current device
- * (256 CUs assumed when no device is present): for each of the *n_workgroups workgroups,
+ * (256 CUs assumed when no device is present), given split_ws_bytes of split workspace:
+ * for each of the *n_workgroups workgroups,
  * the tile it computes (index over (b, h, 128-row m-tile), m-tile fastest), its split
  * index within the tile (the merge order) and its half-open range [j0, j1) of 64-key
  * blocks.  The ranges of a tile's splits partition [0, ceil(S / 64)) in split order.
@@ -181,8 +201,8 @@ int xstage_attn_a2a_plan(int B, int S, int H_local, int D, int* n_workgroups, in
  * sized to each workgroup's CU placement; others use equal ranges.  Host only; the four
  * arrays hold at least `cap` ints (caller-owned); cap < *n_workgroups writes nothing and
  * returns XSTAGE_ERR_INVALID with *n_workgroups set. */
-int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, int cap, int* tile, int* split,
-                             int* j0, int* j1, int* n_workgroups);
+int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, unsigned long long split_ws_bytes,
+                             int cap, int* tile, int* split, int* j0, int* j1, int* n_workgroups);
 
 /* Instrumented xstage_attn_a2a_fwd for the per-tile store-span study ("Results",
  * FlashAttention-A2A: the measured overhead against the completion-coupled counterfactual;
@@ -197,7 +217,8 @@ int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, int cap, int* til
  *   mode 3: as mode 0, but stamp entries [2] and [3] hold the shader-clock counter
  *           (s_memtime) at start and at the end of the key loop, so that
  *           ([3] - [2]) / ([1] - [0]) * xstage_wallclock_hz is the core clock the loop ran at;
- *   stamps: device uint64 [n_workgroups][4 waves][4] (xstage_attn_a2a_plan), caller-owned,
+ *   stamps: device uint64 [n_workgroups][4 waves][4] (xstage_attn_a2a_plan with the same
+ *           split_ws_bytes, or 0 when split_ws is NULL), caller-owned,
  *           8-byte aligned, disjoint from every other argument; per wave, in wall-clock
  *           ticks (xstage_wallclock_hz): start, end of the key loop, last epilogue store
  *           issued (0 if the wave stores nothing: a split that does not merge, rows past S,
@@ -205,7 +226,8 @@ int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, int cap, int* til
  * Other modes are XSTAGE_ERR_INVALID. */
 int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void* const* out_slabs,
                                int B, int S, int H_local, int D, int P, float scale, int mode,
-                               unsigned long long* stamps, void* stream);
+                               unsigned long long* stamps, void* split_ws,
+                               unsigned long long split_ws_bytes, void* stream);
 
 /* Expert-wave grouped GEMM with the combine all-to-all in the Linear-2 epilogue: the
  * stand-in for the interleaved scheduling of "Contributions", MegaMoE (reshaping) item, and

@@ -8,6 +8,19 @@ CANARY = 0x5EED        # guard-zone pattern around each slab
 GUARD = 32             # guard elements (64 bytes) before, between and after slabs
 
 
+_SPLIT_WS = None
+
+
+def split_ws() -> torch.Tensor:
+    """One zero-filled split workspace shared by the GPU tests, large enough for every plan
+    (16 KiB of counters plus 128 MiB of partials): every call leaves the counters it used at zero, so
+    calls of any shape may reuse it one after another on one stream."""
+    global _SPLIT_WS
+    if _SPLIT_WS is None:
+        _SPLIT_WS = torch.zeros((129 << 20,), dtype=torch.uint8, device="cuda")
+    return _SPLIT_WS
+
+
 def to_dev(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 

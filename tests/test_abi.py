@@ -47,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -81,10 +81,13 @@ def slabs(P, base=SLAB0, step=GAP):
     return [base + p * step for p in range(P)]
 
 
-def fwd(L, q=Q, k=K, v=V, sl=None, B=1, S=256, H=2, D=64, P=2, scale=0.125):
+WS = 0x60_0000_0000  # a fake split workspace
+
+
+def fwd(L, q=Q, k=K, v=V, sl=None, B=1, S=256, H=2, D=64, P=2, scale=0.125, ws=None, ws_bytes=0):
     sl = slabs(P) if sl is None else sl
     arr, keep = _lib.ptr_array(sl)
-    return L.xstage_attn_a2a_fwd(q, k, v, arr if sl != "null" else None, B, S, H, D, P, scale, None)
+    return L.xstage_attn_a2a_fwd(q, k, v, arr if sl != "null" else None, B, S, H, D, P, scale, ws, ws_bytes, None)
 
 
 @no_device
@@ -104,7 +107,7 @@ def test_fused_rejects(L, kw, code):
 
 @no_device
 def test_fused_rejects_bad_slabs(L):
-    assert L.xstage_attn_a2a_fwd(Q, K, V, None, 1, 256, 2, 64, 2, 0.125, None) == INVALID
+    assert L.xstage_attn_a2a_fwd(Q, K, V, None, 1, 256, 2, 64, 2, 0.125, None, 0, None) == INVALID
     assert fwd(L, sl=[SLAB0, 0]) == INVALID                       # null slab
     assert fwd(L, sl=[SLAB0, SLAB0 + 16]) == INVALID              # slabs overlap
     assert fwd(L, sl=[SLAB0, Q + 64]) == INVALID                  # slab inside q
@@ -117,13 +120,61 @@ def test_fused_rejects_bad_slabs(L):
 
 
 @no_device
+def test_fused_rejects_bad_split_workspace(L):
+    """The part of the split workspace a launch uses must be aligned and disjoint from every
+    other buffer; an unused workspace (no split, or too small for any) is never touched."""
+    B, S, H, D, P = 1, 4608, 3, 128, 8
+    need = xs.xstage_attn_split_ws_size(B, S, H, D)
+    assert need > 0
+    big = dict(B=B, S=S, H=H, D=D, P=P, sl=slabs(P))
+    assert fwd(L, ws=WS + 8, ws_bytes=need, **big) == INVALID          # misaligned
+    assert fwd(L, ws=Q + 4096, ws_bytes=need, **big) == INVALID        # overlaps q
+    assert fwd(L, ws=V - 256, ws_bytes=need, **big) == INVALID         # runs into v
+    assert fwd(L, ws=SLAB0 + GAP - 512, ws_bytes=need, **big) == INVALID   # runs into slab 2
+    # a workspace inside q that the plan does not use is never touched: the call proceeds to
+    # its other checks (here: a NaN scale)
+    assert fwd(L, ws=Q + 4096, ws_bytes=16, scale=float("nan"), **big) == INVALID
+
+
+def test_split_ws_size_and_plan(L):
+    """The workspace query reports the fastest plan's bytes (counters padded to 256, then the
+    bf16 partial records of every (tile, split) unit); a smaller workspace limits the split
+    count to what fits, none gives no split."""
+    B, S, H, D = 1, 4608, 3, 128
+    n_tiles = B * H * ((S + 127) // 128)
+    nwg, nsp = xs.xstage_attn_a2a_plan(B, S, H, D)
+    rec = 4 * (2 * (D // 32) + 1) * 64 * 16
+    need = xs.xstage_attn_split_ws_size(B, S, H, D)
+    assert need == 16384 + nwg * rec
+    assert xs.xstage_attn_a2a_plan(B, S, H, D, need) == (nwg, nsp)
+    assert xs.xstage_attn_a2a_plan(B, S, H, D, 0) == (n_tiles, 1)
+    assert xs.xstage_attn_a2a_plan(B, S, H, D, need - 1)[1] < nsp
+    for k in range(2, nsp):
+        fit = 16384 + n_tiles * k * rec
+        assert xs.xstage_attn_a2a_plan(B, S, H, D, fit)[1] <= k
+    assert xs.xstage_attn_split_ws_size(1, 1, 1, 64) == 0
+    # large shapes are split within the 128 MiB partial cap
+    assert xs.xstage_attn_split_ws_size(4, 58240, 3, 64) <= (128 << 20) + 16384
+    # more than 4096 tiles: never split (the counter area holds 4096)
+    assert xs.xstage_attn_a2a_plan(8, 65536, 1, 64)[1] == 1
+    n = _lib.ctypes.c_ulonglong(0)
+    assert L.xstage_attn_split_ws_size(1, 256, 2, 80, _lib.ctypes.byref(n)) == UNSUPPORTED
+    assert L.xstage_attn_split_ws_size(0, 256, 2, 64, _lib.ctypes.byref(n)) == INVALID
+    assert L.xstage_attn_split_ws_size(1, 256, 2, 64, None) == INVALID
+
+
+@no_device
 def test_attn_fwd_rejects(L):
-    f = L.xstage_attn_fwd
+    def f(*a):
+        return L.xstage_attn_fwd(*a[:-1], None, 0, a[-1])
+
     assert f(Q, K, V, 0, 1, 256, 2, 64, 0.125, None) == INVALID
     assert f(Q, K, V, K + 32, 1, 256, 2, 64, 0.125, None) == INVALID   # out overlaps k
     assert f(Q, K, V, SLAB0 + 8, 1, 256, 2, 64, 0.125, None) == INVALID
     assert f(Q, K, V, SLAB0, 1, 256, 2, 80, 0.125, None) == UNSUPPORTED
     assert f(Q, K, V, SLAB0, 1, 0, 2, 64, 0.125, None) == INVALID
+    need = xs.xstage_attn_split_ws_size(1, 4608, 3, 128)
+    assert L.xstage_attn_fwd(Q, K, V, SLAB0, 1, 4608, 3, 128, 0.125, SLAB0 + 64, need, None) == INVALID
 
 
 @no_device
@@ -142,7 +193,9 @@ def test_scatter_rejects(L):
 @no_device
 def test_unfused_rejects(L):
     arr, keep = _lib.ptr_array(slabs(2))
-    f = L.xstage_attn_a2a_unfused
+    def f(*a):
+        return L.xstage_attn_a2a_unfused(*a[:-1], None, 0, a[-1])
+
     W = 0x50_0000_0000
     assert f(Q, K, V, 0, arr, 1, 256, 2, 64, 2, 0.125, None) == INVALID
     assert f(Q, K, V, W + 8, arr, 1, 256, 2, 64, 2, 0.125, None) == INVALID
@@ -150,6 +203,9 @@ def test_unfused_rejects(L):
     assert f(Q, K, V, SLAB0 + GAP - 64, arr, 1, 256, 2, 64, 2, 0.125, None) == INVALID  # overlaps slab 1
     assert f(Q, K, V, W, arr, 1, 256, 2, 64, 2, float("nan"), None) == INVALID
     assert f(Q, K, V, W, arr, 1, 256, 2, 64, 3, 0.125, None) == INVALID
+    arr8, keep8 = _lib.ptr_array(slabs(8))
+    need = xs.xstage_attn_split_ws_size(1, 4608, 3, 128)
+    assert L.xstage_attn_a2a_unfused(Q, K, V, W, arr8, 1, 4608, 3, 128, 8, 0.125, W + 4096, need, None) == INVALID
 
 
 def test_plan_counts_workgroups(L):
@@ -159,9 +215,9 @@ def test_plan_counts_workgroups(L):
     nwg, nsp = xs.xstage_attn_a2a_plan(1, 1, 1, 64)
     assert (nwg, nsp) == (1, 1)
     n = _lib.ctypes.c_int(0)
-    assert L.xstage_attn_a2a_plan(1, 256, 2, 80, _lib.ctypes.byref(n), None) == UNSUPPORTED
-    assert L.xstage_attn_a2a_plan(0, 256, 2, 64, _lib.ctypes.byref(n), None) == INVALID
-    assert L.xstage_attn_a2a_plan(1, 256, 2, 64, None, None) == INVALID
+    assert L.xstage_attn_a2a_plan(1, 256, 2, 80, 0, _lib.ctypes.byref(n), None) == UNSUPPORTED
+    assert L.xstage_attn_a2a_plan(0, 256, 2, 64, 0, _lib.ctypes.byref(n), None) == INVALID
+    assert L.xstage_attn_a2a_plan(1, 256, 2, 64, 0, None, None) == INVALID
 
 
 SCHEDULE_SHAPES = [(1, 256, 2, 64), (1, 4608, 3, 128), (1, 4608, 3, 64), (2, 4608, 3, 128), (1, 9216, 3, 128),
@@ -221,10 +277,12 @@ def test_schedule_mixes_placements_in_one_round(L):
 def test_schedule_rejects(L):
     n = _lib.ctypes.c_int(0)
     buf = (_lib.ctypes.c_int * 4)()
-    assert L.xstage_attn_a2a_schedule(1, 4608, 3, 128, 4, buf, buf, buf, buf, _lib.ctypes.byref(n)) == INVALID
+    full = _lib.WS_FULL
+    assert L.xstage_attn_a2a_schedule(1, 4608, 3, 128, full, 4, buf, buf, buf, buf, _lib.ctypes.byref(n)) == INVALID
     assert n.value == xs.xstage_attn_a2a_plan(1, 4608, 3, 128)[0]
-    assert L.xstage_attn_a2a_schedule(1, 256, 2, 64, 0, None, None, None, None, None) == INVALID
-    assert L.xstage_attn_a2a_schedule(1, 256, 2, 80, 0, None, None, None, None, _lib.ctypes.byref(n)) == UNSUPPORTED
+    assert L.xstage_attn_a2a_schedule(1, 256, 2, 64, full, 0, None, None, None, None, None) == INVALID
+    assert L.xstage_attn_a2a_schedule(1, 256, 2, 80, full, 0, None, None, None, None,
+                                      _lib.ctypes.byref(n)) == UNSUPPORTED
 
 
 STAMPS = 0x50_0000_0000
@@ -233,7 +291,9 @@ STAMPS = 0x50_0000_0000
 @no_device
 def test_traced_rejects(L):
     arr, keep = _lib.ptr_array(slabs(2))
-    f = L.xstage_attn_a2a_fwd_traced
+    def f(*a):
+        return L.xstage_attn_a2a_fwd_traced(*a[:-1], None, 0, a[-1])
+
     args = (Q, K, V, arr, 1, 256, 2, 64, 2, 0.125)
     assert f(*args, 4, STAMPS, None) == INVALID                # unknown mode
     assert f(*args, -1, STAMPS, None) == INVALID
@@ -247,7 +307,9 @@ def test_traced_rejects(L):
 
 @no_device
 def test_strided_rejects(L):
-    f = L.xstage_attn_a2a_fwd_strided
+    def f(*a):
+        return L.xstage_attn_a2a_fwd_strided(*a[:-1], None, 0, a[-1])
+
     arr, keep = _lib.ptr_array(slabs(2))
 
     def call(H=2, P=2, H_dst=8, h0=4, q=Q, sl=arr, S=256, scale=0.125):
@@ -269,7 +331,9 @@ def test_strided_rejects(L):
 
 @no_device
 def test_ulysses_rejects(L):
-    f = L.xstage_ulysses_attn_fwd
+    def f(*a):
+        return L.xstage_ulysses_attn_fwd(*a[:-1], None, 0, a[-1])
+
     P = 4
     qs = [0x10_0000_0000 + p * GAP for p in range(P)]
     ks = [0x20_0000_0000 + p * GAP for p in range(P)]
@@ -437,17 +501,21 @@ def test_serial_ulysses_rejects(L):
     args = lambda **kw: dict(q=arr(qs), k=arr(ks), v=arr(vs), ws=WS, d=arr(ds), B=1, S=256, H=8, Hl=2, h0=2,
                              D=64, P=P, scale=0.125) | kw
     call = lambda a: u(a["q"], a["k"], a["v"], a["ws"], a["d"], a["B"], a["S"], a["H"], a["Hl"], a["h0"], a["D"],
-                       a["P"], a["scale"], None)
+                       a["P"], a["scale"], a.get("sws"), a.get("swsb", 0), None)
     assert call(args(ws=0)) == INVALID
     assert call(args(ws=ks[2] + 16)) == INVALID                  # workspace inside a shard
     assert call(args(d=arr([ds[0], ds[1], WS + 64, ds[3]]))) == INVALID  # output inside the workspace
     assert call(args(scale=float("nan"))) == INVALID
     assert call(args(h0=7)) == INVALID
     assert call(args(D=96)) == UNSUPPORTED
+    # a split workspace that the (split) plan uses may not overlap the staging workspace
+    need = xs.xstage_attn_split_ws_size(1, 4608, 2, 64)
+    assert need > 0
+    assert call(args(S=4608, sws=WS + 64, swsb=need)) == INVALID
     # K/V-staged layer: same argument list, workspace of 2 x [B, S, H_local, D]
     kv = L.xstage_ulysses_attn_fwd_kv_staged
     kcall = lambda a: kv(a["q"], a["k"], a["v"], a["ws"], a["d"], a["B"], a["S"], a["H"], a["Hl"], a["h0"], a["D"],
-                         a["P"], a["scale"], None)
+                         a["P"], a["scale"], a.get("sws"), a.get("swsb", 0), None)
     tl = 1 * 256 * 2 * 64 * 2
     assert kcall(args(ws=0)) == INVALID
     assert kcall(args(ws=WS + 8)) == INVALID                     # misaligned workspace

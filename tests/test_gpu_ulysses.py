@@ -6,8 +6,8 @@
 * xstage_ulysses_attn_fwd: inputs are P sequence shards of all H heads (separate
   allocations); the output must equal gathering the rank's heads into contiguous q, k, v
   and calling the strided path, bit for bit; values against the oracle's Ulysses layer
-  (oracle.ulysses_attention: explicit gather, fp64 attention, explicit scatter), full at
-  small shapes and on sampled query rows at the FLUX-1024 and video groups; shard sizes
+  (oracle.ulysses_attention: explicit gather, fp64 attention, explicit scatter), every
+  query row at every shape up to the FLUX-1024 and video groups; shard sizes
   that are odd or below one 64-key block make key blocks straddle shards;
 * xstage_ulysses_attn_fwd_kv_staged (K and V gathered into a workspace, Q read in place)
   equals xstage_ulysses_attn_fwd bit for bit at every layer shape;
@@ -23,7 +23,7 @@ import torch
 import attention_ulysses_a2a_amd as xs
 import oracle
 from synth import Workload, make_inputs, make_placement_probe
-from tests.gpu_util import NAN_BF16, GuardedSlabs, to_dev
+from tests.gpu_util import split_ws, NAN_BF16, GuardedSlabs, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -76,9 +76,9 @@ def test_strided_destination(B, S, H, D, P, Hd, h0):
     qb, kb, vb = make_inputs(w)
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
     plain = GuardedSlabs(P, B, S // P, H, D)
-    xs.xstage_attn_a2a_fwd(q, k, v, plain.views, w.scale)
+    xs.xstage_attn_a2a_fwd(q, k, v, plain.views, w.scale, split_ws=split_ws())
     full = GuardedSlabs(P, B, S // P, Hd, D)
-    xs.xstage_attn_a2a_fwd_strided(q, k, v, full.views, h0, w.scale)
+    xs.xstage_attn_a2a_fwd_strided(q, k, v, full.views, h0, w.scale, split_ws=split_ws())
     torch.cuda.synchronize()
     assert full.guards_intact()
     got = full.slabs_host()
@@ -87,7 +87,7 @@ def test_strided_destination(B, S, H, D, P, Hd, h0):
     # probe: exact output V, through the strided epilogue
     pq, pk, pv = make_placement_probe(B, S, H, D, w.scale)
     probe = GuardedSlabs(P, B, S // P, Hd, D)
-    xs.xstage_attn_a2a_fwd_strided(to_dev(pq), to_dev(pk), to_dev(pv), probe.views, h0, w.scale)
+    xs.xstage_attn_a2a_fwd_strided(to_dev(pq), to_dev(pk), to_dev(pv), probe.views, h0, w.scale, split_ws=split_ws())
     torch.cuda.synchronize()
     assert probe.guards_intact()
     assert np.array_equal(probe.slabs_host()[:, :, :, h0:h0 + H], oracle.ulysses_scatter(pv, P))
@@ -99,8 +99,8 @@ ULYSSES = [
     (2, 1000, 4, 2, 0, 128, 8, True),     # 125-row shards: key blocks straddle shards
     (1, 64, 2, 1, 1, 128, 8, True),       # 8-row shards: one key block spans all 8
     (1, 999, 3, 1, 1, 64, 3, True),       # 333-row shards, D = 64
-    (1, 4608, 24, 3, 15, 128, 8, False),  # FLUX-1024 group, rank 5
-    (1, 32760, 40, 5, 15, 128, 8, False), # video group, rank 3: 4095-row shards, key tail 56
+    (1, 4608, 24, 3, 15, 128, 8, True),   # FLUX-1024 group, rank 5
+    (1, 32760, 40, 5, 15, 128, 8, True),  # video group, rank 3: 4095-row shards, key tail 56
 ]
 
 
@@ -111,15 +111,15 @@ def test_ulysses_layer(B, S, H, Hl, h0, D, P, full):
     qb, kb, vb = make_inputs(w)
     qs, ks, vs = ([to_dev(x) for x in shards_of(t, P)] for t in (qb, kb, vb))
     out = GuardedSlabs(P, B, S // P, H, D)
-    xs.xstage_ulysses_attn_fwd(qs, ks, vs, out.views, Hl, h0, w.scale)
+    xs.xstage_ulysses_attn_fwd(qs, ks, vs, out.views, Hl, h0, w.scale, split_ws=split_ws())
     # the same heads gathered into contiguous tensors, through the strided path
     ref = GuardedSlabs(P, B, S // P, H, D)
     qc, kc, vc = (to_dev(np.ascontiguousarray(t[:, :, h0:h0 + Hl])) for t in (qb, kb, vb))
-    xs.xstage_attn_a2a_fwd_strided(qc, kc, vc, ref.views, h0, w.scale)
+    xs.xstage_attn_a2a_fwd_strided(qc, kc, vc, ref.views, h0, w.scale, split_ws=split_ws())
     # K and V staged in a workspace, Q read from the shards
     staged = GuardedSlabs(P, B, S // P, H, D)
     ws = torch.full((2, B, S, Hl, D), float("nan"), dtype=torch.bfloat16, device="cuda")
-    xs.xstage_ulysses_attn_fwd_kv_staged(qs, ks, vs, ws, staged.views, Hl, h0, w.scale)
+    xs.xstage_ulysses_attn_fwd_kv_staged(qs, ks, vs, ws, staged.views, Hl, h0, w.scale, split_ws=split_ws())
     torch.cuda.synchronize()
     assert out.guards_intact() and staged.guards_intact()
     got = out.slabs_host()
@@ -143,10 +143,10 @@ def test_ulysses_placement_probe(B, S, H, Hl, h0, D, P):
     pq, pk, pv = make_placement_probe(B, S, H, D, scale)
     qs, ks, vs = ([to_dev(x) for x in shards_of(t, P)] for t in (pq, pk, pv))
     out = GuardedSlabs(P, B, S // P, H, D)
-    xs.xstage_ulysses_attn_fwd(qs, ks, vs, out.views, Hl, h0, scale)
+    xs.xstage_ulysses_attn_fwd(qs, ks, vs, out.views, Hl, h0, scale, split_ws=split_ws())
     staged = GuardedSlabs(P, B, S // P, H, D)
     ws = torch.empty((2, B, S, Hl, D), dtype=torch.bfloat16, device="cuda")
-    xs.xstage_ulysses_attn_fwd_kv_staged(qs, ks, vs, ws, staged.views, Hl, h0, scale)
+    xs.xstage_ulysses_attn_fwd_kv_staged(qs, ks, vs, ws, staged.views, Hl, h0, scale, split_ws=split_ws())
     torch.cuda.synchronize()
     assert out.guards_intact() and staged.guards_intact()
     got = out.slabs_host()
@@ -162,8 +162,8 @@ def test_bound_ulysses_equals_direct():
     stacked = [to_dev(np.stack(shards_of(t, P))) for t in (qb, kb, vb)]  # [P, B, S/P, H, D]
     a = GuardedSlabs(P, B, S // P, H, D)
     b = GuardedSlabs(P, B, S // P, H, D)
-    xs.xstage_ulysses_attn_fwd(*stacked, a.views, Hl, h0, w.scale)
-    f = xs.bind("xstage_ulysses_attn_fwd", *stacked, b.views, Hl, h0, w.scale)
+    xs.xstage_ulysses_attn_fwd(*stacked, a.views, Hl, h0, w.scale, split_ws=split_ws())
+    f = xs.bind("xstage_ulysses_attn_fwd", *stacked, b.views, Hl, h0, w.scale, split_ws=split_ws())
     f()
     f()
     torch.cuda.synchronize()
@@ -208,10 +208,10 @@ def test_ulysses_unfused_equals_fused(B, S, H, Hl, h0, D, P):
     qb, kb, vb = make_inputs(w)
     qs, ks, vs = ([to_dev(x) for x in shards_of(t, P)] for t in (qb, kb, vb))
     fused = GuardedSlabs(P, B, S // P, H, D)
-    xs.xstage_ulysses_attn_fwd(qs, ks, vs, fused.views, Hl, h0, w.scale)
+    xs.xstage_ulysses_attn_fwd(qs, ks, vs, fused.views, Hl, h0, w.scale, split_ws=split_ws())
     serial = GuardedSlabs(P, B, S // P, H, D)
     ws = torch.empty((4, B, S, Hl, D), dtype=torch.bfloat16, device="cuda")
-    xs.xstage_ulysses_attn_unfused(qs, ks, vs, ws, serial.views, Hl, h0, w.scale)
+    xs.xstage_ulysses_attn_unfused(qs, ks, vs, ws, serial.views, Hl, h0, w.scale, split_ws=split_ws())
     torch.cuda.synchronize()
     assert serial.guards_intact()
     got = serial.slabs_host()
