@@ -35,6 +35,7 @@ __all__ = [
     "xstage_attn_a2a_fwd",
     "xstage_attn_split_ws_size",
     "split_workspace",
+    "xstage_attn_a2a_fwd_noalloc",
     "xstage_attn_fwd",
     "xstage_a2a_scatter",
     "xstage_attn_a2a_unfused",
@@ -269,7 +270,16 @@ def _m_ulysses_attn_fwd_kv_staged(q_src, k_src, v_src, workspace, out_dst, H_loc
     return _ulysses_ws_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, split_ws, stream, 2)
 
 
+def _m_attn_a2a_fwd_noalloc(q, k, v, out_slabs, scale=None, stream=None):
+    B, S, H, D = _qkv(q, k, v)
+    ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
+    arr, keep = ptr_array(ptrs)
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), _stream_of(q, stream))
+    return call, (q, k, v, out_slabs, keep), q.device
+
+
 _MARSHAL = {
+    "xstage_attn_a2a_fwd_noalloc": _m_attn_a2a_fwd_noalloc,
     "xstage_attn_a2a_fwd": _m_attn_a2a_fwd,
     "xstage_attn_fwd": _m_attn_fwd,
     "xstage_a2a_scatter": _m_a2a_scatter,
@@ -297,6 +307,12 @@ def xstage_attn_a2a_fwd(q, k, v, out_slabs, scale=None, split_ws=None, stream=No
     [B, S/P, H_local, D] or one [P, B, S/P, H_local, D] tensor); ``split_ws``: optional
     caller-owned split workspace (``split_workspace``); see include/xstage.h."""
     _invoke("xstage_attn_a2a_fwd", q, k, v, out_slabs, scale=scale, split_ws=split_ws, stream=stream)
+
+
+def xstage_attn_a2a_fwd_noalloc(q, k, v, out_slabs, scale=None, stream=None) -> None:
+    """xstage_attn_a2a_fwd with the split workspace in the library's static device array (no
+    allocation by anyone); see include/xstage.h."""
+    _invoke("xstage_attn_a2a_fwd_noalloc", q, k, v, out_slabs, scale=scale, stream=stream)
 
 
 def xstage_attn_fwd(q, k, v, out, scale=None, split_ws=None, stream=None) -> None:

@@ -77,6 +77,7 @@ _WS = [_vp, _u64]  # split_ws, split_ws_bytes
 SIGNATURES = {
     "xstage_attn_a2a_fwd": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),
     "xstage_attn_split_ws_size": (_i, [_i, _i, _i, _i, ctypes.POINTER(_u64)]),
+    "xstage_attn_a2a_fwd_noalloc": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f, _vp]),
     "xstage_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f] + _WS + [_vp]),
     "xstage_a2a_scatter": (_i, [_vp, _PP, _i, _i, _i, _i, _i, _vp]),
     "xstage_attn_a2a_unfused": (_i, [_vp, _vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libxstage.so")
 
-SOURCES = ["api.hip", "attn_a2a.hip", "moe_waves.hip", "scatter_bg.hip", "workspace.hip"]
+SOURCES = ["api.hip", "attn_a2a.hip", "moe_waves.hip", "noalloc.hip", "scatter_bg.hip", "workspace.hip"]
 
 # Packed fp32 VALU forms are disabled on purpose: the compiler must not emit them.
 HIPCC_FLAGS = [

@@ -81,6 +81,21 @@ int xstage_attn_a2a_fwd(const void* q, const void* k, const void* v, void* const
                         int B, int S, int H_local, int D, int P, float scale, void* split_ws,
                         unsigned long long split_ws_bytes, void* stream);
 
+/* xstage_attn_a2a_fwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, hosts that forbid allocation):
+ * the call never allocates.  Its split partials and arrival counters live in a 32 MiB
+ * static device array of the library, one copy per GPU, held until the process ends; the
+ * first call on a device looks up that copy's address and zeroes its counters with a fill
+ * kernel on `stream`, and every call leaves them at zero.  The key-split count is the one
+ * xstage_attn_a2a_fwd chooses with a 32 MiB workspace (the FLUX-1024 share's fastest plan
+ * fits; longer shapes split less), so results equal that call's bit for bit; a plan that
+ * would need more than the array holds returns XSTAGE_ERR_UNSUPPORTED.  All calls on one
+ * GPU share its array: calls that may overlap on one GPU (different streams or threads)
+ * race.  Arguments, requirements and result otherwise as for xstage_attn_a2a_fwd. */
+int xstage_attn_a2a_fwd_noalloc(const void* q, const void* k, const void* v,
+                                void* const* out_slabs, int B, int S, int H_local, int D, int P,
+                                float scale, void* stream);
+
 /* Bytes of split workspace the attention entry points use for this shape at full speed
  * (see the split workspace convention above); 0 when the shape is not split.  Host only. */
 int xstage_attn_split_ws_size(int B, int S, int H_local, int D, unsigned long long* bytes);
