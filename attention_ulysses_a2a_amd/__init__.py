@@ -502,16 +502,24 @@ def xstage_moe_waves_run(x, w1, w2, h, expert_offsets, dst_slab, dst_row, outs, 
 
 
 def xstage_burst_gap_run(K, V_bytes, gap_fma_iters, rounds, dst, stamps, n_dst_sets=1, nontemporal=False,
-                         stream=None) -> None:
-    """Burst-Gap store microbenchmark; ``stamps`` is an int64 device tensor of K*rounds*3 entries."""
+                         sync=None, sync_timeout_ticks=0, stream=None) -> None:
+    """Burst-Gap store microbenchmark; ``stamps`` is an int64 device tensor of K*rounds*3
+    entries; ``sync`` (optional) a zero-filled int32 device tensor of ``rounds`` entries that
+    turns on the per-round start barrier across producers (bounded by sync_timeout_ticks)."""
     import torch
 
-    if stamps.numel() < K * rounds * 3 or stamps.element_size() != 8 or not stamps.is_cuda:
-        raise ValueError("stamps must be a device tensor of K*rounds*3 64-bit entries")
-    if V_bytes and (dst is None or dst.numel() * dst.element_size() < n_dst_sets * V_bytes):
-        raise ValueError("dst must hold n_dst_sets * V_bytes bytes")
+    _dev_tensor(stamps, "stamps", min_bytes=K * rounds * 3 * 8, bf16=False)
+    if stamps.element_size() != 8:
+        raise ValueError("stamps must be a 64-bit tensor")
+    if V_bytes:
+        if dst is None:
+            raise ValueError("dst must hold n_dst_sets * V_bytes bytes")
+        _dev_tensor(dst, "dst", device=stamps.device, min_bytes=n_dst_sets * V_bytes, bf16=False)
+    if sync is not None:
+        _dev_tensor(sync, "sync", device=stamps.device, min_bytes=rounds * 4, bf16=False)
     p = BGParams(int(K), int(rounds), int(n_dst_sets), int(bool(nontemporal)), int(V_bytes), int(gap_fma_iters),
-                 dst.data_ptr() if dst is not None else None, stamps.data_ptr())
+                 dst.data_ptr() if dst is not None else None, stamps.data_ptr(),
+                 sync.data_ptr() if sync is not None else None, int(sync_timeout_ticks))
     with torch.cuda.device(stamps.device):
         st = lib().xstage_burst_gap_run(ctypes.byref(p), _stream_of(stamps, stream))
     _check(st, "xstage_burst_gap_run")

@@ -63,6 +63,8 @@ class BGParams(ctypes.Structure):
         ("gap_fma_iters", ctypes.c_uint),
         ("dst", ctypes.c_void_p),
         ("stamps", ctypes.c_void_p),
+        ("sync", ctypes.c_void_p),
+        ("sync_timeout_ticks", ctypes.c_ulonglong),
     ]
 
 

@@ -80,3 +80,55 @@ def fit(points, drain_margin: float = 1.1):
     res["capacity_reading"] = {"c_s": c, "f1_Bps": f1, "R_Bps": r, "Q_bytes": q,
                                "rel_err_median": float(np.median(relq)), "rel_err_max": float(relq.max())}
     return res
+
+
+def fit_isolated(V, T, T0, R=None, margin: float = 1.5):
+    """Capacity Q from bursts issued on an empty queue (capacity reading: T = max(T0, (V - Q)/R)).
+
+    Points with T > margin * T0 lie on T = (V - Q) / R: a least-squares line T = a + b V
+    gives R_iso = 1/b and Q_iso = -a/b; with a drain rate R from the periodic sweep,
+    Q = median(V - R T)."""
+    V, T, T0 = (np.asarray(x, float) for x in (V, T, T0))
+    use = T > margin * T0
+    res = {"n_used": int(use.sum())}
+    if len(set(V[use].tolist())) < 2:
+        return res
+    b, a = np.polyfit(V[use], T[use], 1)
+    res["R_iso_Bps"] = float(1.0 / b)
+    res["Q_iso_bytes"] = float(-a / b)
+    if R is not None:
+        res["Q_bytes_at_R"] = float(np.median(V[use] - R * T[use]))
+    return res
+
+
+def fit_synchronized(large, isolated, c, f1, K, margin: float = 1.5):
+    """Fits of the series whose producers start every round together (one aggregate burst).
+
+    large: (V, G, T) of periodic bursts; isolated: (V, T[, start spread]) of bursts on a
+    drained queue; T0 = c + V / (K f1), the backpressure-free issue time from the
+    unsynchronised sweep (plus, for an isolated burst, the spread of its producers' starts).
+    * R_agg: least squares of V = R T over the zero-gap periodic points;
+    * the printed formula max(T0, V/R_agg - G) and the capacity reading
+      max(T0, V/R_agg - min(G, Q/R_agg)) against the periodic points with G > 0 (median
+      relative error each; Q from the isolated fit);
+    * the isolated fit (``fit_isolated``) with R = R_agg."""
+    L = np.asarray(large, float)
+    V, G, T = L.T
+    z = G == 0
+    R = float(np.dot(V[z], V[z]) / np.dot(V[z], T[z]))
+    iso = np.asarray(isolated, float)
+    # An aggregate burst cannot be issued before its last producer has started and issued
+    # its own share freely: its free time is the start spread plus c + V / (K f1).
+    spread = iso[:, 2] if iso.shape[1] > 2 else 0.0
+    t0_iso = c + iso[:, 0] / (K * f1) + spread
+    fi = fit_isolated(iso[:, 0], iso[:, 1], t0_iso, R=R, margin=margin)
+    res = {"R_agg_Bps": R, "isolated": fi}
+    Q = fi.get("Q_bytes_at_R")
+    g = G > 0
+    t0 = c + V[g] / (K * f1)
+    page = np.maximum(t0, V[g] / R - G[g])
+    res["page_formula_rel_err_median"] = float(np.median(np.abs(T[g] - page) / T[g]))
+    if Q is not None:
+        cap = np.maximum(t0, V[g] / R - np.minimum(G[g], max(Q, 0.0) / R))
+        res["capacity_reading_rel_err_median"] = float(np.median(np.abs(T[g] - cap) / T[g]))
+    return res

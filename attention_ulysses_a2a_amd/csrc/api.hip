@@ -464,6 +464,14 @@ int xstage_burst_gap_run(const xstage_bg_params_t* p, void* stream) {
   if (p->stamps == nullptr || (reinterpret_cast<uintptr_t>(p->stamps) & 7u) != 0) return XSTAGE_ERR_INVALID;
   if (p->V_bytes % (4096ull * (unsigned long long)p->K) != 0) return XSTAGE_ERR_INVALID;
   if (p->V_bytes > 0 && (p->dst == nullptr || !aligned16(p->dst))) return XSTAGE_ERR_INVALID;
+  if (p->sync != nullptr) {
+    if ((reinterpret_cast<uintptr_t>(p->sync) & 3u) != 0) return XSTAGE_ERR_INVALID;
+    if (p->sync_timeout_ticks < 1 || p->sync_timeout_ticks > 1000000000ull) return XSTAGE_ERR_INVALID;
+    const Range sr = range_of(p->sync, (unsigned long long)p->rounds * 4ull);
+    if (overlaps(sr, range_of(p->stamps, (unsigned long long)p->K * p->rounds * 24ull))) return XSTAGE_ERR_INVALID;
+    if (p->V_bytes > 0 && overlaps(sr, range_of(p->dst, (unsigned long long)p->n_dst_sets * p->V_bytes)))
+      return XSTAGE_ERR_INVALID;
+  }
   return launch_burst_gap(*p, static_cast<hipStream_t>(stream));
 }
 

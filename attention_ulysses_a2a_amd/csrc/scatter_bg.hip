@@ -138,6 +138,9 @@ struct BGArgs {
   int rounds;
   int n_sets;
   unsigned gap;
+  int K;
+  uint32_t* sync;                  // per-round arrival counts (nullptr: no start barrier)
+  unsigned long long sync_timeout;  // wall-clock ticks a producer waits at most per round
 };
 
 __device__ __forceinline__ unsigned long long wall_ticks() { return __builtin_amdgcn_s_memrealtime(); }
@@ -149,6 +152,19 @@ __global__ __launch_bounds__(256) void burst_gap_kernel(const BGArgs a) {
   float x = (float)tid * 1e-3f;
   for (int r = 0; r < a.rounds; ++r) {
     uint8_t* base = a.dst + (size_t)(r % a.n_sets) * a.V + (size_t)wg * a.share;
+    if (a.sync != nullptr) {
+      // Start barrier across producers: count this producer in, then wait until all K
+      // are in or the timeout passes.  The count is an agent-scope atomic and the polls are
+      // device-scope (sc1) vector loads; the wall clock always advances, so the wait ends.
+      __builtin_amdgcn_s_barrier();
+      if (tid == 0) {
+        __hip_atomic_fetch_add(&a.sync[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(a.sync, (short)0, a.rounds * 4, 0x00020000);
+        const unsigned long long t_end = wall_ticks() + a.sync_timeout;
+        while (__builtin_amdgcn_raw_buffer_load_b32(rs, r * 4, 0, 16) < (uint32_t)a.K && wall_ticks() < t_end)
+          __builtin_amdgcn_s_sleep(1);
+      }
+    }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const unsigned long long t0 = wall_ticks();
@@ -195,6 +211,9 @@ int launch_burst_gap(const xstage_bg_params_t& p, hipStream_t stream) {
   a.rounds = p.rounds;
   a.n_sets = p.n_dst_sets;
   a.gap = p.gap_fma_iters;
+  a.K = p.K;
+  a.sync = p.sync;
+  a.sync_timeout = p.sync_timeout_ticks;
   if (p.nontemporal)
     hipLaunchKernelGGL(burst_gap_kernel<true>, dim3(p.K), dim3(256), 0, stream, a);
   else

@@ -310,6 +310,14 @@ int xstage_moe_waves_plan(int E, const int* expert_offsets, int d_model, int d_f
  *           [0] burst start (all waves of the producer at the start barrier),
  *           [1] last store of the burst issued by every wave (no wait for completion),
  *           [2] end of the gap; in the last round, taken after the wait for completion.
+ *   sync:   NULL, or device uint32 [rounds], zero-filled, 4-byte aligned, disjoint from dst
+ *           and stamps: then every round starts with a start barrier across the K
+ *           producers (each adds 1 to sync[round] and waits until all K have arrived or
+ *           sync_timeout_ticks wall-clock ticks have passed, whichever comes first), so
+ *           that the K bursts of a round start together and their union is one aggregate
+ *           burst of V bytes; the wait always ends (the timeout bounds it).  Without sync
+ *           the producers' rounds drift apart.  sync_timeout_ticks: 1 .. 10^9 when sync
+ *           is set.
  *   V_bytes must be a multiple of K * 4096 (each producer stores whole 4 KiB rows of
  *   16-byte lanes); V_bytes = 0 runs the gap alone (calibration).  1 <= K <= 4096,
  *   1 <= rounds <= 65536, n_dst_sets >= 1, nontemporal in {0, 1}. */
@@ -322,6 +330,8 @@ typedef struct {
   unsigned int gap_fma_iters;
   void* dst;
   unsigned long long* stamps;
+  unsigned int* sync;
+  unsigned long long sync_timeout_ticks;
 } xstage_bg_params_t;
 
 int xstage_burst_gap_run(const xstage_bg_params_t* p, void* stream);

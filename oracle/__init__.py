@@ -21,8 +21,9 @@ Inference", technical summary):
   intermediate, Linear-2, then the combine all-to-all's row placement) in float64.
 * ``burst_gap``: the Burst-Gap issue-time model of the "Methodology" section,
   T_iss(G; K, V) = max(T0_iss(K, V), V / R - G), its two regimes, a labelled fluid-queue
-  reading that gives the capacity Q a role, and the parameter fit used on microbenchmark
-  sweeps ("Contributions", characterisation item).
+  reading that gives the capacity Q a role (with its isolated-burst limit, from which Q is
+  read), and the parameter fits used on microbenchmark sweeps ("Contributions",
+  characterisation item).
 
 Pins (tests under ``tests/test_oracle_*.py``): brute force with exact summation on tiny
 inputs, torch's float64 scaled_dot_product_attention, closed-form invariants, hand-computed
@@ -43,8 +44,10 @@ from .ulysses import pre_gather, scatter_heads, ulysses_attention  # noqa: F401
 from .moe import moe_layer  # noqa: F401
 from .burst_gap import (  # noqa: F401
     fit_burst_gap,
+    fit_isolated,
     regime,
     t0_linear,
     t_iss,
     t_iss_fluid,
+    t_iss_isolated,
 )

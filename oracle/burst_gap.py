@@ -60,6 +60,38 @@ def t0_linear(K, V, c, f1):
     return np.float64(c) + np.asarray(V, dtype=np.float64) / (np.asarray(K, dtype=np.float64) * np.float64(f1))
 
 
+def t_iss_isolated(T0, V, R, Q):
+    """Capacity reading for a burst that starts on an empty queue (the previous burst drained
+    long before): the first Q bytes are absorbed, the rest issue at the drain rate, so
+    T_iss = max(T0, (V - Q) / R).  This is the G -> infinity limit of ``t_iss_fluid``."""
+    V = np.asarray(V, dtype=np.float64)
+    return np.maximum(np.asarray(T0, dtype=np.float64), (V - np.float64(Q)) / np.float64(R))
+
+
+def fit_isolated(V, T, T0, R=None, margin=1.5):
+    """Capacity Q (and a drain rate) from isolated bursts, per the capacity reading.
+
+    V, T: volumes (bytes) and issue times (s) of bursts issued on an empty queue; T0: their
+    backpressure-free issue times.  Points with T > margin * T0 lie on T = (V - Q) / R:
+    * a least-squares line T = a + b V over those points gives R_iso = 1 / b and
+      Q_iso = -a / b (both from the isolated bursts alone);
+    * with a drain rate R measured elsewhere (the drain branch of periodic bursts),
+      Q = median(V - R T) over the same points.
+    Needs at least two distinct volumes above the margin."""
+    V = np.asarray(V, dtype=np.float64)
+    T = np.asarray(T, dtype=np.float64)
+    sel = T > margin * np.asarray(T0, dtype=np.float64)
+    out = {"n_used": int(sel.sum())}
+    if len(set(V[sel].tolist())) < 2:
+        return out
+    b, a = np.polyfit(V[sel], T[sel], 1)
+    out["R_iso"] = float(1.0 / b)
+    out["Q_iso"] = float(-a / b)
+    if R is not None:
+        out["Q"] = float(np.median(V[sel] - np.float64(R) * T[sel]))
+    return out
+
+
 def fit_burst_gap(points, drain_margin=1.1):
     """Fit the Burst-Gap parameters to measured (K, V_bytes, G_s, T_iss_s) points.
 

@@ -368,7 +368,7 @@ def test_burst_gap_rejects(L):
 
     def run(**kw):
         base = dict(K=64, rounds=8, n_dst_sets=1, nontemporal=0, V_bytes=1 << 20, gap_fma_iters=10,
-                    dst=SLAB0, stamps=Q)
+                    dst=SLAB0, stamps=Q, sync=None, sync_timeout_ticks=0)
         base.update(kw)
         p = _lib.BGParams(**base)
         return L.xstage_burst_gap_run(ctypes.byref(p), None)
@@ -384,6 +384,11 @@ def test_burst_gap_rejects(L):
     assert run(V_bytes=(1 << 20) + 4096) == INVALID   # not a multiple of K * 4096
     assert run(dst=0) == INVALID
     assert run(dst=SLAB0 + 8) == INVALID
+    assert run(sync=0x70_0000_0002, sync_timeout_ticks=100) == INVALID       # misaligned
+    assert run(sync=0x70_0000_0000, sync_timeout_ticks=0) == INVALID         # no bound on the wait
+    assert run(sync=0x70_0000_0000, sync_timeout_ticks=10 ** 10) == INVALID  # bound above 10^9 ticks
+    assert run(sync=Q + 8, sync_timeout_ticks=100) == INVALID                # inside the stamps
+    assert run(sync=SLAB0 + 4096, sync_timeout_ticks=100) == INVALID         # inside dst
 
 
 @no_device

@@ -88,3 +88,74 @@ def test_pacing_chunks_rejects():
     assert L.xstage_bg_pacing_chunks(float("nan"), 1.0, 1.0, 1.0, 1.0, 1.0, 4, None) == 0
     assert L.xstage_bg_pacing_chunks(1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 0, None) == 0      # c_max < 1
     assert L.xstage_bg_pacing_chunks(1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1, None) == 1
+
+
+def test_product_isolated_fit_matches_oracle():
+    """The sweep's isolated-burst fit and the oracle's, on bursts drawn from the capacity reading."""
+    rng = np.random.default_rng(7)
+    R, Q, c, f1, K = 6.8e12, 140 * 2 ** 20, 9e-8, 130e9, 256
+    V = np.repeat(np.array([32, 64, 128, 256, 384, 512, 768, 1024]) * 2 ** 20, 3).astype(float)
+    T0 = oracle.t0_linear(K, V, c, f1)
+    T = oracle.t_iss_isolated(T0, V, R, Q) * (1 + 0.005 * rng.standard_normal(V.size))
+    mine = bg_model.fit_isolated(V, T, T0, R=R)
+    ref = oracle.fit_isolated(V, T, T0, R=R)
+    assert abs(mine["R_iso_Bps"] / ref["R_iso"] - 1) < 1e-9
+    assert abs(mine["Q_iso_bytes"] / ref["Q_iso"] - 1) < 1e-9
+    assert abs(mine["Q_bytes_at_R"] / ref["Q"] - 1) < 1e-9
+    assert abs(mine["Q_iso_bytes"] / Q - 1) < 0.05
+
+
+def test_sweep_summary_renders_every_series():
+    """The markdown summary of a sweep's JSON lines (host logic only, synthetic records)."""
+    import json
+
+    from attention_ulysses_a2a_amd import bg_sweep
+
+    lines = [json.dumps({"bg_calibration": {"wallclock_hz": 1e8, "gap_ns_per_fma_iter": 15.0}})]
+    for variant in ("hot", "cold", "large"):
+        for G in (0, 1):
+            lines.append(json.dumps({"bg": {"variant": variant, "K": 256, "V_MiB": 64, "G_us": G, "T_iss_us": 5.0 - G,
+                                            "T_iss_p10_us": 4.0, "T_iss_p90_us": 6.0, "span_us": 5.0,
+                                            "period_us": 6.0, "R_direct_GBps": 7000.0 if G == 0 else None}}))
+        lines.append(json.dumps({"bg_fit": {"variant": variant, "R": 7e12, "n_drain": 2, "n_points": 2,
+                                            "capacity_reading": {"R_Bps": 7.1e12, "Q_bytes": 150 * 2 ** 20,
+                                                                 "f1_Bps": 1.3e11, "c_s": 8.6e-8,
+                                                                 "rel_err_median": 0.03}, "T0_us": {}}}))
+    # isolated bursts on T = (V - 8 MiB) / 7 TB/s, well above their free time
+    for vm in (64, 256, 1024):
+        t = (vm - 8) * 2 ** 20 / 7e12 * 1e6
+        lines.append(json.dumps({"bg": {"variant": "isolated", "K": 256, "V_MiB": vm, "G_us": 200.0,
+                                        "T0_free_us": 1.0, "T_iss_us": t, "T_iss_p10_us": t, "T_iss_p90_us": t,
+                                        "start_spread_us": 0.4}}))
+    lines.append(json.dumps({"bg_sync_fit": {"K": 256, "free_c_s": 8.6e-8, "free_f1_Bps": 1.3e11,
+                                             "R_agg_Bps": 7e12, "page_formula_rel_err_median": 0.5,
+                                             "capacity_reading_rel_err_median": 0.02,
+                                             "isolated": {"n_used": 5, "R_iso_Bps": 7e12, "Q_iso_bytes": 150 * 2 ** 20,
+                                                          "Q_bytes_at_R": 151 * 2 ** 20}}}))
+    lines.append(json.dumps({"bg_copy": {"write_GBps": 2500.0, "read_write_GBps": 5000.0, "s_per_call": 2e-4,
+                                         "bytes_written": 2 ** 29}}))
+    md = bg_sweep.summarize(lines)
+    for head in ("## hot destinations", "## cold destinations", "## large bursts", "## isolated bursts",
+                 "## plain copy"):
+        assert head in md
+    assert "Q_iso = 8.0 MiB" in md and "R_iso = 7.00 TB/s" in md
+    assert "| 256 | 64 | 5.00 | 4.00 | 7000 |" in md and "R_agg = 13.42 TB/s" in md
+
+
+def test_synchronized_fit_prefers_the_capacity_reading():
+    """Aggregate bursts drawn from the capacity reading with a small Q: the fit recovers R and Q,
+    and the printed formula (which lets every gap shorten the burst) fits the gapped points worse."""
+    R, Q, c, f1, K = 5.9e12, 8 * 2 ** 20, 8.6e-8, 130e9, 256
+    large = []
+    for vm in (128, 256, 512, 1024):
+        V = vm * 2 ** 20
+        for G in (0, 10e-6, 20e-6, 40e-6, 80e-6, 160e-6):
+            large.append((V, G, float(oracle.t_iss_fluid(G, oracle.t0_linear(K, V, c, f1), V, R, Q))))
+    iso = []
+    for vm in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
+        V = vm * 2 ** 20
+        iso.append((V, float(oracle.t_iss_isolated(oracle.t0_linear(K, V, c, f1), V, R, Q))))
+    f = bg_model.fit_synchronized(large, iso, c, f1, K)
+    assert abs(f["R_agg_Bps"] / R - 1) < 0.01
+    assert abs(f["isolated"]["Q_bytes_at_R"] / Q - 1) < 0.01
+    assert f["capacity_reading_rel_err_median"] < 0.01 < f["page_formula_rel_err_median"]

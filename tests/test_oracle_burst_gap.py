@@ -124,3 +124,66 @@ def test_fit_recovers_fluid_parameters():
     assert abs(fl["f1"] / f1 - 1) < 0.05
     assert abs(fl["c"] / c - 1) < 0.2
     assert fl["rel_err_median"] < 0.01
+
+
+def test_t0_linear_hand_values():
+    """T0 read as a fixed cost c plus one producer's share V/K at its free rate f1 (hand-evaluated)."""
+    # 4 producers, 8 MB: each moves 2 MB at 1 GB/s = 2 ms, plus 1 us
+    assert abs(float(oracle.t0_linear(4, 8e6, 1e-6, 1e9)) - 2.001e-3) < 1e-15
+    # 256 producers, 64 MiB: 262144 B each at 130 GB/s = 2.016492 us, plus 86 ns
+    assert abs(float(oracle.t0_linear(256, 64 * 2 ** 20, 86e-9, 130e9)) - 2.102492308e-6) < 1e-15
+    # broadcasting over (K, V)
+    got = oracle.t0_linear(np.array([1, 2]), np.array([1e9, 1e9]), 0.0, 1e9)
+    assert np.array_equal(got, np.array([1.0, 0.5]))
+
+
+def test_t0_linear_matches_brute_force_producers():
+    """K producers, each starting after c and issuing its V/K share in fixed-size pieces at f1
+    (time-stepped): the last one finishes at t0_linear(K, V, c, f1)."""
+    for K, V, c, f1 in ((3, 3.0e6, 2e-6, 5e8), (8, 6.4e6, 0.0, 2e9), (1, 1e6, 1e-6, 1e9)):
+        dt = 1e-7
+        share = V / K
+        finish = []
+        for _ in range(K):
+            t, left = c, share
+            while left > 1e-9:
+                left -= min(left, f1 * dt)
+                t += dt
+            finish.append(t)
+        assert abs(max(finish) - float(oracle.t0_linear(K, V, c, f1))) <= 2 * dt
+
+
+def test_isolated_limit_of_the_fluid_reading():
+    """A burst on an empty queue: the fluid reading at gaps past Q/R is max(T0, (V - Q)/R)."""
+    T0, R, Q = 2e-6, 7e12, 150 * 2 ** 20
+    for V in (2 ** 27, 2 ** 28, 2 ** 29, 2 ** 30):
+        for G in (Q / R, 2 * Q / R, 1e-3):
+            assert abs(float(oracle.t_iss_fluid(G, T0, V, R, Q)) - float(oracle.t_iss_isolated(T0, V, R, Q))) < 1e-15
+    assert float(oracle.t_iss_isolated(T0, 2 ** 20, R, Q)) == T0        # absorbed entirely
+    assert abs(float(oracle.t_iss_isolated(T0, 2 ** 30, R, Q)) - (2 ** 30 - Q) / R) < 1e-15
+
+
+def test_simulated_isolated_bursts_agree():
+    """The time-stepped queue, started empty, issues one burst in max(T0, (V - Q)/R) (fast producer)."""
+    T0, R, Q = 0.01, 1.0, 0.5
+    for V in (0.4, 1.0, 2.0):
+        sim, dt = simulate_queue(V, T0, R, Q, G=100.0, periods=1, steps=4000)
+        assert abs(sim - float(oracle.t_iss_isolated(T0, V, R, Q))) <= 5 * dt + 1e-9
+
+
+def test_fit_isolated_recovers_capacity_and_rate():
+    """Isolated bursts drawn from the capacity reading (with noise): the line through the
+    points above T0 gives R and Q; with R given, Q is the median of V - R T."""
+    rng = np.random.default_rng(3)
+    R, Q, c, f1, K = 6.5e12, 160 * 2 ** 20, 1e-7, 130e9, 256
+    V = np.repeat(np.array([32, 64, 128, 256, 384, 512, 768, 1024]) * 2 ** 20, 4).astype(float)
+    T0 = oracle.t0_linear(K, V, c, f1)
+    T = oracle.t_iss_isolated(T0, V, R, Q) * (1 + 0.01 * rng.standard_normal(V.size))
+    f = oracle.fit_isolated(V, T, T0)
+    assert abs(f["R_iso"] / R - 1) < 0.03 and abs(f["Q_iso"] / Q - 1) < 0.08
+    g = oracle.fit_isolated(V, T, T0, R=R)
+    assert abs(g["Q"] / Q - 1) < 0.08
+    # bursts that all fit in the capacity identify nothing
+    small = np.array([1, 2, 4, 8]) * 2 ** 20
+    t0s = oracle.t0_linear(K, small, c, f1)
+    assert "Q_iso" not in oracle.fit_isolated(small, oracle.t_iss_isolated(t0s, small, R, Q), t0s)
