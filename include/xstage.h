@@ -185,14 +185,16 @@ int xstage_ulysses_attn_fwd_kv_staged(const void* const* q_src, const void* cons
                                       int h0, int D, int P, float scale, void* split_ws,
                                       unsigned long long split_ws_bytes, void* stream);
 
-/* The separate all-to-all send step of the serial baseline: copies a contiguous
+/* The separate all-to-all send step of the serial baseline ("Results", FlashAttention-A2A:
+ * serial execution runs attention, then the all-to-all): copies a contiguous
  * [B, S, H_local, D] tensor into the P slabs.  Slabs must not overlap `in` or each other. */
 int xstage_a2a_scatter(const void* in, void* const* out_slabs, int B, int S, int H_local,
                        int D, int P, void* stream);
 
-/* Serial baseline: xstage_attn_fwd into `workspace` ([B, S, H_local, D], caller-owned),
- * then xstage_a2a_scatter into the slabs, both on `stream`.  Same result as
- * xstage_attn_a2a_fwd, bit for bit. */
+/* Serial baseline ("Results", FlashAttention-A2A: the fused kernel is measured against
+ * attention followed by a separate all-to-all): xstage_attn_fwd into `workspace`
+ * ([B, S, H_local, D], caller-owned), then xstage_a2a_scatter into the slabs, both on
+ * `stream`.  Same result as xstage_attn_a2a_fwd, bit for bit. */
 int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* workspace,
                             void* const* out_slabs, int B, int S, int H_local, int D, int P,
                             float scale, void* split_ws, unsigned long long split_ws_bytes,
@@ -337,8 +339,9 @@ typedef struct {
 int xstage_burst_gap_run(const xstage_bg_params_t* p, void* stream);
 
 /* Frequency of the device wall clock used by the microbenchmark stamps, in Hz
- * (hipDeviceAttributeWallClockRate of the current device).  The only entry point that
- * queries the device. */
+ * (hipDeviceAttributeWallClockRate of the current device), which turns the Burst-Gap
+ * stamps into the issue times of "Methodology".  The only entry point that queries the
+ * device. */
 int xstage_wallclock_hz(double* hz);
 
 /* Burst-Gap issue time in seconds ("Methodology"): max(T0, V/R - G), with V in bytes and R
@@ -358,7 +361,8 @@ double xstage_bg_t_iss(double G_s, double T0_s, double V_bytes, double R_bytes_p
 int xstage_bg_pacing_chunks(double V_bytes, double G_s, double a_s, double f1_Bps, double R_Bps, double Q_bytes,
                             int c_max, double* t_visible_s);
 
-/* Static string naming a status code. */
+/* Static string naming a status code returned by any entry point above (plumbing of this
+ * C ABI; the pages describe no API). */
 const char* xstage_status_str(int status);
 
 #ifdef __cplusplus
