@@ -32,3 +32,18 @@ def test_loop_clock_from_stamps():
     st = np.array([[0, 1000, 5, 20005], [10, 1010, 0, 18000], [0, 100, 0, 99999]], dtype=np.int64)
     assert xstage_study.loop_clock_ghz(st, hz) == pytest.approx(1.9)
     assert xstage_study.loop_clock_ghz(st[2:], hz) is None
+
+
+def test_study_summary_table():
+    """The markdown table of a study's JSON lines (host logic, a synthetic record)."""
+    import json
+
+    rec = {"S": 4608, "H_local": 3, "D": 128, "P": 8, "workgroups": 432, "key_splits": 4, "rounds": 0.84,
+           "t_attn_us": 38.6, "t_fused_us": 38.5, "t_traced_us": 39.0, "t_nostore_us": 38.2, "t_coupled_us": 39.1,
+           "overhead_fused_vs_attn_us": -0.1, "overhead_fused_vs_nostore_us": 0.3,
+           "overhead_coupled_vs_nostore_us": 0.9, "epilogue_span_us_median": 5.3, "epilogue_span_us_p90": 6.0,
+           "drain_span_us_median": 0.12, "drain_span_us_p90": 0.16, "coupled_model_us": 38.6,
+           "loop_clock_ghz": 1.98, "iterations": 1300}
+    md = xstage_study.summarize([json.dumps(rec)], "abc")
+    assert "`abc`" in md
+    assert "| 4608 | 432 | 4 | 0.84 | 38.6 | 38.5 | -0.10 | 39.0 | 38.2 | 39.1 | +0.80 | +0.90 | 5.30 | 0.12 / 0.16 | 38.6 | 1.98 |" in md
