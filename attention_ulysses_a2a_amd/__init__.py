@@ -48,6 +48,8 @@ __all__ = [
     "xstage_attn_a2a_plan",
     "xstage_attn_a2a_schedule",
     "xstage_attn_a2a_fwd_traced",
+    "xstage_attn_a2a_fwd_paced",
+    "xstage_attn_a2a_paced_plan",
     "xstage_moe_waves_run",
     "xstage_moe_waves_plan",
     "xstage_burst_gap_run",
@@ -270,6 +272,15 @@ def _m_ulysses_attn_fwd_kv_staged(q_src, k_src, v_src, workspace, out_dst, H_loc
     return _ulysses_ws_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, split_ws, stream, 2)
 
 
+def _m_attn_a2a_fwd_paced(q, k, v, out_slabs, chunks, scale=None, stream=None):
+    B, S, H, D = _qkv(q, k, v)
+    ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
+    arr, keep = ptr_array(ptrs)
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), int(chunks),
+            _stream_of(q, stream))
+    return call, (q, k, v, out_slabs, keep), q.device
+
+
 def _m_attn_a2a_fwd_noalloc(q, k, v, out_slabs, scale=None, stream=None):
     B, S, H, D = _qkv(q, k, v)
     ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
@@ -285,6 +296,7 @@ _MARSHAL = {
     "xstage_a2a_scatter": _m_a2a_scatter,
     "xstage_attn_a2a_unfused": _m_attn_a2a_unfused,
     "xstage_attn_a2a_fwd_traced": _m_attn_a2a_fwd_traced,
+    "xstage_attn_a2a_fwd_paced": _m_attn_a2a_fwd_paced,
     "xstage_attn_a2a_fwd_strided": _m_attn_a2a_fwd_strided,
     "xstage_ulysses_attn_fwd": _m_ulysses_attn_fwd,
     "xstage_ulysses_attn_unfused": _m_ulysses_attn_unfused,
@@ -337,6 +349,21 @@ def xstage_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, spl
     include/xstage.h."""
     _invoke("xstage_attn_a2a_fwd_traced", q, k, v, out_slabs, mode, stamps, scale=scale, split_ws=split_ws,
             stream=stream)
+
+
+def xstage_attn_a2a_fwd_paced(q, k, v, out_slabs, chunks, scale=None, stream=None) -> None:
+    """Paced persistent fused call: each finished tile's rows are issued in ``chunks`` chunks
+    over the next tile's first key-loop iterations; slabs as xstage_attn_a2a_fwd's without
+    split workspace, bit for bit; see include/xstage.h."""
+    _invoke("xstage_attn_a2a_fwd_paced", q, k, v, out_slabs, chunks, scale=scale, stream=stream)
+
+
+def xstage_attn_a2a_paced_plan(B: int, S: int, H_local: int, D: int):
+    """(n_workgroups, n_tiles) of the paced launch for this shape on the current device."""
+    nwg, nt = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().xstage_attn_a2a_paced_plan(int(B), int(S), int(H_local), int(D), ctypes.byref(nwg),
+                                            ctypes.byref(nt)), "xstage_attn_a2a_paced_plan")
+    return nwg.value, nt.value
 
 
 def xstage_attn_a2a_fwd_strided(q, k, v, out_dst, h_dst0, scale=None, split_ws=None, stream=None) -> None:
@@ -573,8 +600,9 @@ def bind(name: str, *args, **kwargs) -> _Bound:
     current stream of the tensors' device unless ``stream`` is given), and the calls must be
     made with that device current.  Supported: the attention entry points
     (xstage_attn_a2a_fwd, xstage_attn_fwd, xstage_a2a_scatter, xstage_attn_a2a_unfused,
-    xstage_attn_a2a_fwd_traced, xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd,
-    xstage_ulysses_attn_unfused, xstage_ulysses_attn_fwd_kv_staged) and
+    xstage_attn_a2a_fwd_traced, xstage_attn_a2a_fwd_paced, xstage_attn_a2a_fwd_strided,
+    xstage_ulysses_attn_fwd, xstage_ulysses_attn_unfused, xstage_ulysses_attn_fwd_kv_staged,
+    xstage_attn_a2a_fwd_noalloc) and
     xstage_moe_waves_run, with the same arguments as the functions.
     """
     import torch

@@ -6,19 +6,13 @@
 
 #include <vector>
 
+#include "attn_a2a.hpp"
 #include "common.hpp"
 #include "moe_waves.hpp"
 #include "validate.hpp"
 #include "workspace.hpp"
 
 namespace xstage {
-int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
-                    int P, float scale, void* ws, unsigned long long ws_bytes, hipStream_t stream, int mode = 0,
-                    unsigned long long* stamps = nullptr, const Layout* layout = nullptr);
-int attn_workgroups(int B, int S, int H, int D, unsigned long long ws_bytes, int* n_split);
-unsigned long long attn_ws_used(int B, int S, int H, int D, unsigned long long ws_bytes);
-int attn_schedule(int B, int S, int H, int D, unsigned long long ws_bytes, int cap, int* tile, int* split, int* j0,
-                  int* j1);
 int launch_scatter(const void* in, const SlabTable& slabs, int B, int S, int H, int D, int P, hipStream_t stream);
 int launch_slice_copy(const void* const* src, int src_sharded, int src_w, int src_off, void* const* dst,
                       int dst_sharded, int dst_w, int dst_off, int B, int S, int H_local, int D, int P,
@@ -363,6 +357,28 @@ int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void
   if (st != XSTAGE_OK) return st;
   return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale, split_ws, split_ws_bytes,
                          static_cast<hipStream_t>(stream), 1 + mode, stamps);
+}
+
+int xstage_attn_a2a_fwd_paced(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
+                              int H_local, int D, int P, float scale, int chunks, void* stream) {
+  const int st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, nullptr, 0, nullptr, 0);
+  if (st != XSTAGE_OK) return st;
+  const int stores_per_lane = 32 * (D / 8) / 64;  // a wave's 32 rows in 16-byte stores: 8 (D=128), 4 (D=64)
+  if (chunks < 1 || chunks > stores_per_lane || stores_per_lane % chunks != 0) return XSTAGE_ERR_INVALID;
+  return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale, nullptr, 0,
+                         static_cast<hipStream_t>(stream), kAttnModePaced, nullptr, nullptr, chunks);
+}
+
+int xstage_attn_a2a_paced_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_tiles) {
+  if (n_workgroups == nullptr || n_tiles == nullptr) return XSTAGE_ERR_INVALID;
+  const int st = check_shape(B, S, H_local, D, 1);
+  if (st != XSTAGE_OK) return st;
+  int wg = 0;
+  const int tiles = attn_paced_workgroups(B, S, H_local, D, &wg);
+  if (wg < 1) return XSTAGE_ERR_HIP;
+  *n_workgroups = wg;
+  *n_tiles = tiles;
+  return XSTAGE_OK;
 }
 
 static int check_moe_shape(int E, const int* offsets, int d_model, int d_ff, int epw, int schedule,

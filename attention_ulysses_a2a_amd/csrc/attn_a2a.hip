@@ -22,8 +22,10 @@
 //     16-byte chunks straight into the slab owning that sequence row.  The stores are not
 //     waited on.
 #include <algorithm>
+#include <atomic>
 #include <math.h>
 
+#include "attn_a2a.hpp"
 #include "common.hpp"
 #include "validate.hpp"
 #include "workspace.hpp"
@@ -76,6 +78,7 @@ struct AttnArgs {
   uint32_t qflip;    // 0x80008000 for a negative scale: Q is negated on load
   void* partial;      // split partials: [tile][split][wave][chunk][64 lanes] (n_split > 1)
   int partial_bytes;  // bytes of the partial area (< 2^31)
+  int pace_chunks;    // paced mode: chunks per output tile (a divisor of the stores per lane)
   uint32_t* counters;  // per-tile arrival counters, zero between launches (n_split > 1)
   unsigned long long* stamps;  // traced modes: [workgroup][wave][4] wall-clock ticks
   int clock_stamps;  // traced modes: entries 2, 3 hold shader-clock ticks at start / loop end
@@ -87,7 +90,12 @@ struct AttnArgs {
 // kCoupled makes every wave wait for its stores before it ends (the completion-coupled
 // counterfactual: the issuer blocks until its stores are visible); kNoStore issues no output
 // store at all (the unbounded-asynchronous bound: stores cost nothing; nothing is written).
-enum AttnMode { kRun = 0, kTraced = 1, kCoupled = 2, kNoStore = 3 };
+// kPaced is the paced persistent mode: each workgroup runs several tiles in turn, keeps the
+// finished tile's rows in LDS and issues them in pace_chunks chunks, one at the start of each
+// of the next tile's first key-loop iterations (two 64-key blocks each), so that the store
+// burst is spread over the next tile's compute; the last tile's rows are issued at the end.
+// Splits are not used (one unit per tile), and the results equal the unsplit product path's.
+enum AttnMode { kRun = 0, kTraced = 1, kCoupled = 2, kNoStore = 3, kPaced = kAttnModePaced };
 // Host-side launch mode: kTraced with shader-clock stamps in entries 2 and 3.
 constexpr int kTracedClock = 4;
 
@@ -114,7 +122,7 @@ struct NoSrc {};
 enum SrcMode { kPlain = 0, kShards = 1, kShardQ = 2 };
 
 template <int D, int MODE, int SRC>
-__global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, const UnitTable tab,
+__global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(const AttnArgs a, const UnitTable tab,
                                                           const std::conditional_t<SRC != kPlain, SrcTable, NoSrc> src) {
   // The body names device-only types (the buffer resource), which the host pass of a
   // template cannot instantiate; the host pass only needs the launch signature.
@@ -131,6 +139,11 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   auto sp = [&](int slot_byte) -> char* {
     return slot_byte < C::BLKB ? lds_k0 : slot_byte < 2 * C::BLKB ? lds_k1 : slot_byte < 3 * C::BLKB ? lds_v0 : lds_v1;
   };
+  constexpr bool kPace = MODE == kPaced;
+  constexpr bool kStamped = MODE == kTraced || MODE == kCoupled || MODE == kNoStore;
+  // Paced mode: the finished tile's rows (4 waves x 32 rows, restaged as in the epilogue)
+  // wait here while the next tile's key loop runs.
+  __shared__ __attribute__((aligned(16))) char lds_out[kPace ? 4 * 32 * C::ROWB : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,13 +152,13 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   // Traced modes: each stamp is stored (by lane 0) as soon as it is taken, so that no
   // stamp stays live across the key loop and the merge.
   auto stamp = [&](int slot, unsigned long long v) {
-    if constexpr (MODE != kRun) {
+    if constexpr (kStamped) {
       if (lane == 0) a.stamps[((size_t)blockIdx.x * 4 + w) * 4 + slot] = v;
     }
   };
   // Entries 2 and 3 start at 0: a workgroup that stores no output (a split that does not
   // merge, rows past S, the no-store mode) leaves them so.
-  if constexpr (MODE != kRun) {
+  if constexpr (kStamped) {
     stamp(0, __builtin_amdgcn_s_memrealtime());
     if (a.clock_stamps) {
       stamp(2, __builtin_amdgcn_s_memtime());
@@ -156,6 +169,41 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   }
 
   const int nkv = (a.S + C::BN - 1) / C::BN;
+
+  // Paced mode: the tile whose rows wait in lds_out (wave-uniform; pend_row0 < 0: none) and
+  // the next of its chunks to issue.  issue_pending(n) issues chunks pend_next .. n-1: each
+  // is stores [k * per, (k + 1) * per) of the wave's 8 (D = 128) or 4 (D = 64) 16-byte
+  // stores per lane, every row to the slab that owns it.
+  constexpr int NST = 32 * C::CH / 64;  // 16-byte stores per lane for a wave's 32 rows
+  int pend_row0 = -1, pend_b = 0, pend_h = 0, pend_next = 0;
+  auto issue_pending = [&](int upto) {
+    if constexpr (kPace) {
+      if (pend_row0 < 0) return;
+      const char* const pst = lds_out + __builtin_amdgcn_readfirstlane(w) * 32 * C::ROWB;
+      const int per = NST / a.pace_chunks;
+      const int p_lo = pend_row0 / a.S_P, p_hi = min(pend_row0 + 31, a.S - 1) / a.S_P;
+      for (; pend_next < upto; ++pend_next) {
+        for (int i = pend_next * per; i < (pend_next + 1) * per; ++i) {
+          const int lin = i * 64 + lane;
+          const int row = lin / C::CH, ch = lin % C::CH;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(pst + row * C::ROWB + ((ch ^ swz<D>(row)) << 4));
+          const int s_row = pend_row0 + row;
+          const int p = s_row / a.S_P;
+          const int r = s_row - p * a.S_P;
+          const uint32_t off = (((uint32_t)pend_b * a.S_P + r) * a.dst_hs + a.dst_h0 + pend_h) * D + ch * 8;
+          // slab pointers are read at wave-uniform indices only
+          for (int pp = p_lo; pp <= p_hi; ++pp)
+            if (s_row < a.S && p == pp) *(g_u32x4*)(uniform_ptr(a.slabs.p[pp]) + off) = val;
+        }
+      }
+    }
+  };
+
+  // One pass per unit; the paced mode runs units blockIdx.x, blockIdx.x + gridDim.x, ...
+  for (int unit = blockIdx.x;; unit += gridDim.x) {
+  if constexpr (kPace) {
+    if (unit != (int)blockIdx.x) __syncthreads();  // the previous unit's LDS reads are done
+  }
   // This workgroup's tile, split and key-block range [j0, j1).  One-round launches take
   // them from the unit table (kernel arguments: one scalar load, issued with the others).
   // Otherwise the order is XCD-aware: workgroup i runs on XCD i % 8; each XCD gets a
@@ -163,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   // and the splits are uniform.
   int tile, split, j0, j1;
   {
-    const int i = blockIdx.x;
+    const int i = unit;
     const uint32_t e = tab.e[i < kUnitTableCap ? i : 0];
     if (a.use_table) {
       tile = e & 1023;
@@ -483,6 +531,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   };
   int j = j0;
   for (; j + 2 < j1; j += 2) {
+    if constexpr (kPace) issue_pending(min(pend_next + 1, a.pace_chunks));
     step(j, 0, s_a, s_b);
     step(j + 1, 1, s_b, s_a);
   }
@@ -503,14 +552,14 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
     last_block(j, s_a, VSLOT0);
   }
 
-  if constexpr (MODE != kRun) {
+  if constexpr (kStamped) {
     stamp(1, __builtin_amdgcn_s_memrealtime());
     if (a.clock_stamps) stamp(3, __builtin_amdgcn_s_memtime());
   }
 
   // ---- key-range splits: every split stores its partial (O, m, l); the last to arrive
   // merges them (rescaling by exp2(m_s - m)) and runs the epilogue for the tile.
-  if (a.n_split > 1) {
+  if (!kPace && a.n_split > 1) {
     __shared__ int last_flag;
     // One record per (tile, split, wave), in lane-major 16-byte chunks: the unnormalised O
     // rounded to bf16 (two chunks per 32-wide d tile, accumulator registers 0..7 and 8..15),
@@ -618,8 +667,10 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
 
   // ---- epilogue: normalise, bf16, restage per wave, store rows into their slabs ----------
   const float inv = 1.0f / sum_with_partner32(l_run);
-  // wave-private [32][D] restage area in the K slots (free after the loop)
-  char* stage = (w < 2 ? lds_k0 : lds_k1) + (w & 1) * 32 * C::ROWB;
+  // wave-private [32][D] restage area in the K slots (free after the loop); paced mode: in
+  // lds_out, once the previous tile's rows have all been issued from there
+  if constexpr (kPace) issue_pending(a.pace_chunks);
+  char* stage = kPace ? lds_out + w * 32 * C::ROWB : (w < 2 ? lds_k0 : lds_k1) + (w & 1) * 32 * C::ROWB;
   {
     const int n = lane & 31;
     const int sw = swz<D>(n);
@@ -635,11 +686,17 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
   }
   __builtin_amdgcn_wave_barrier();
 
+  if constexpr (kPace) {
+    const int row0 = m0 + wu * 32;
+    pend_row0 = row0 < S ? row0 : -1;
+    pend_b = b;
+    pend_h = h;
+    pend_next = 0;
+  } else {
   // Destination of each restaged row.  The wave's 32 rows are consecutive sequence rows, so
   // unless a slab holds fewer than 32 rows they touch at most two slabs, whose pointers are
   // read once as wave-uniform (scalar) values: the stores then issue back to back with no
   // wait between them.  Tiny slabs (fewer than 32 rows) take a per-row-pointer path.
-  constexpr int NST = 32 * C::CH / 64;  // 16-byte stores per lane
   // wu: this wave's index as a wave-uniform value (defined with the loads above)
   const int row0 = m0 + wu * 32;
   if (row0 >= S || MODE == kNoStore) return;
@@ -685,7 +742,7 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       }
     }
   }
-  if constexpr (MODE != kRun) {
+  if constexpr (kStamped) {
     const unsigned long long t_issued = __builtin_amdgcn_s_memrealtime();
     unsigned long long t_done = 0;
     if constexpr (MODE == kCoupled) {
@@ -697,13 +754,47 @@ __global__ __launch_bounds__(256, 2) void attn_a2a_kernel(const AttnArgs a, cons
       stamp(3, t_done);
     }
   }
+  }  // end of the non-paced epilogue
+  if constexpr (!kPace) {
+    break;
+  } else {
+    if (unit + (int)gridDim.x >= a.n_units) break;
+  }
+  }  // units
+  // paced mode: the last tile's rows
+  if constexpr (kPace) issue_pending(a.pace_chunks);
 #endif
+}
+
+// Workgroups of the paced kernel that fit on one CU at once (LDS-bound: one), cached per D
+// (it does not depend on the device); 0 if the query fails.
+template <int D>
+static int paced_per_cu() {
+  static std::atomic<int> per_cu{0};
+  int n = per_cu.load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_a2a_kernel<D, kPaced, kPlain>, AttnCfg<D>::THREADS, 0) !=
+            hipSuccess ||
+        n < 1)
+      return 0;
+    per_cu.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Workgroups of a paced launch (each runs tiles i, i + n, i + 2n, ...); returns the tile count
+// and sets *n_wg (0 if the occupancy query failed).
+int attn_paced_workgroups(int B, int S, int H, int D, int* n_wg) {
+  const int n_tiles = B * H * ((S + 127) / 128);
+  const int per = D == 128 ? paced_per_cu<128>() : paced_per_cu<64>();
+  *n_wg = per < 1 ? 0 : std::min(n_tiles, cu_count() * per);
+  return n_tiles;
 }
 
 template <int D>
 static int launch_attn(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H,
                        int P, float scale, const SplitPlan& plan, int mode, unsigned long long* stamps,
-                       const Layout& lay, hipStream_t stream) {
+                       const Layout& lay, int pace_chunks, hipStream_t stream) {
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -722,6 +813,7 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.partial = plan.partial;
   a.partial_bytes = (int)((size_t)a.n_units * partial_bytes_per_unit(D));
   a.counters = plan.counters;
+  a.pace_chunks = pace_chunks;
   a.stamps = stamps;
   a.clock_stamps = mode == kTracedClock;
   if (mode == kTracedClock) mode = kTraced;
@@ -736,6 +828,14 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   const UnitTable& t = tab ? *tab : kNoTable;
   const dim3 grid(a.n_units), block(AttnCfg<D>::THREADS);
   const NoSrc none;
+  if (mode == kPaced) {  // persistent: as many workgroups as fit at once, each runs several tiles
+    if (lay.src || plan.n_split != 1) return XSTAGE_ERR_INVALID;
+    const int n = paced_per_cu<D>();
+    if (n < 1) return XSTAGE_ERR_HIP;
+    const dim3 pgrid(std::min(a.n_units, cu_count() * n));
+    hipLaunchKernelGGL((attn_a2a_kernel<D, kPaced, kPlain>), pgrid, block, 0, stream, a, t, none);
+    return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
+  }
   if (lay.src) {  // shards: product mode only
     if (mode != kRun) return XSTAGE_ERR_INVALID;
     if (lay.kv_contiguous)
@@ -800,7 +900,7 @@ int attn_schedule(int B, int S, int H, int D, unsigned long long ws_bytes, int c
 
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
                     int P, float scale, void* ws, unsigned long long ws_bytes, hipStream_t stream, int mode,
-                    unsigned long long* stamps, const Layout* layout) {
+                    unsigned long long* stamps, const Layout* layout, int pace_chunks) {
   static const Layout kDefaultLayout;
   const Layout& lay = layout ? *layout : kDefaultLayout;
   const int n_tiles = B * H * ((S + 127) / 128);
@@ -811,8 +911,8 @@ int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable
     plan.counters = static_cast<uint32_t*>(ws);
     plan.partial = static_cast<char*>(ws) + kCounterAreaBytes;
   }
-  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, stream);
-  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, stream);
+  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, pace_chunks, stream);
+  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, pace_chunks, stream);
 }
 
 }  // namespace xstage

@@ -11,16 +11,12 @@
 // calls that may overlap on one GPU (different streams, threads) race.
 #include <mutex>
 
+#include "attn_a2a.hpp"
 #include "common.hpp"
 #include "validate.hpp"
 #include "workspace.hpp"
 
 namespace xstage {
-
-int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
-                    int P, float scale, void* ws, unsigned long long ws_bytes, hipStream_t stream, int mode,
-                    unsigned long long* stamps, const Layout* layout);
-unsigned long long attn_ws_used(int B, int S, int H, int D, unsigned long long ws_bytes);
 
 namespace {
 

@@ -9,6 +9,13 @@
 
 namespace xstage {
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int cu_count();
+
+// Launch mode of the attention kernel's paced persistent variant (the kernel's own modes
+// 0..4 are the product and the traced variants).
+constexpr int kAttnModePaced = 5;
+
 struct SplitPlan {
   int n_split = 1;          // key-range splits per (b, h, m-tile); 1 = no merge
   int kvb_per_split = 0;    // 64-key blocks per split (the last split may get fewer)

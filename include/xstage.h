@@ -246,6 +246,32 @@ int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void
                                unsigned long long* stamps, void* split_ws,
                                unsigned long long split_ws_bytes, void* stream);
 
+/* Paced fused attention + all-to-all: the burst-shaping use of the Burst-Gap model
+ * ("Significance": the model as a way to shape the communication bursts and hide their
+ * issuer-side cost; "Methodology": a burst of V followed by a gap G of compute) applied to
+ * the epilogue of the fused kernel ("Contributions", FlashAttention-A2A item: the tile's
+ * owner issues its stores and goes on with the next tile's query loop).  A persistent
+ * launch: xstage_attn_a2a_paced_plan's n_workgroups workgroups (as many as fit on the
+ * device at once) each compute tiles i, i + n_workgroups, ...; a finished tile's rows wait
+ * in LDS and are issued in `chunks` equal chunks, one at the start of each of the next
+ * tile's first key-loop iterations (128 keys each); chunks a short next tile has no
+ * iteration for, and the last tile's rows, are issued after its loop.  chunks = 1 issues the
+ * whole tile at once, at the next tile's first iteration.
+ *   chunks: 1, 2, 4 or 8 for D = 128 (a wave's 32 rows are 8 16-byte stores per lane);
+ *           1, 2 or 4 for D = 64; anything else is XSTAGE_ERR_INVALID.
+ * Same arguments otherwise as xstage_attn_a2a_fwd, no key splits and no workspace: the slab
+ * contents equal xstage_attn_a2a_fwd's with split_ws = NULL, bit for bit, for every
+ * `chunks`.  Never synchronizes or allocates; argument errors as xstage_attn_a2a_fwd. */
+int xstage_attn_a2a_fwd_paced(const void* q, const void* k, const void* v, void* const* out_slabs,
+                              int B, int S, int H_local, int D, int P, float scale, int chunks,
+                              void* stream);
+
+/* Decomposition of xstage_attn_a2a_fwd_paced for this shape on the current device:
+ * *n_tiles = B * H_local * ceil(S / 128) tiles over *n_workgroups persistent workgroups.
+ * Host only (queries the device's occupancy once per D); XSTAGE_ERR_HIP if that query
+ * fails. */
+int xstage_attn_a2a_paced_plan(int B, int S, int H_local, int D, int* n_workgroups, int* n_tiles);
+
 /* Expert-wave grouped GEMM with the combine all-to-all in the Linear-2 epilogue: the
  * stand-in for the interleaved scheduling of "Contributions", MegaMoE (reshaping) item, and
  * "Results", MegaMoE optimisation.  E experts on this GPU; expert e owns the token rows

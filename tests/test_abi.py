@@ -47,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -103,6 +103,34 @@ def fwd(L, q=Q, k=K, v=V, sl=None, B=1, S=256, H=2, D=64, P=2, scale=0.125, ws=N
 ])
 def test_fused_rejects(L, kw, code):
     assert fwd(L, **kw) == code
+
+
+def paced(L, chunks, q=Q, B=1, S=256, H=2, D=128, P=2, scale=0.125):
+    arr, keep = _lib.ptr_array(slabs(P))
+    return L.xstage_attn_a2a_fwd_paced(q, K, V, arr, B, S, H, D, P, scale, chunks, None)
+
+
+@no_device
+@pytest.mark.parametrize("kw,code", [
+    (dict(chunks=0), INVALID), (dict(chunks=-1), INVALID), (dict(chunks=3), INVALID),
+    (dict(chunks=16), INVALID), (dict(chunks=8, D=64), INVALID), (dict(chunks=6, D=64), INVALID),
+    (dict(chunks=1, q=0), INVALID), (dict(chunks=2, S=1001, P=8), INVALID),
+    (dict(chunks=4, D=96), UNSUPPORTED), (dict(chunks=1, scale=float("nan")), INVALID),
+])
+def test_paced_rejects(L, kw, code):
+    assert paced(L, **kw) == code
+
+
+@no_device
+def test_paced_plan_needs_a_device(L):
+    import ctypes
+
+    n, t = ctypes.c_int(-1), ctypes.c_int(-1)
+    assert L.xstage_attn_a2a_paced_plan(1, 256, 2, 128, None, ctypes.byref(t)) == INVALID
+    assert L.xstage_attn_a2a_paced_plan(0, 256, 2, 128, ctypes.byref(n), ctypes.byref(t)) == INVALID
+    assert L.xstage_attn_a2a_paced_plan(1, 256, 2, 96, ctypes.byref(n), ctypes.byref(t)) == UNSUPPORTED
+    # the occupancy query has no device to ask
+    assert L.xstage_attn_a2a_paced_plan(1, 256, 2, 128, ctypes.byref(n), ctypes.byref(t)) == _lib.XSTAGE_ERR_HIP
 
 
 @no_device
