@@ -50,6 +50,8 @@ __all__ = [
     "xstage_attn_a2a_fwd_traced",
     "xstage_attn_a2a_fwd_paced",
     "xstage_attn_a2a_paced_plan",
+    "xstage_attn_a2a_fwd_nsplit",
+    "xstage_attn_nsplit_ws_size",
     "xstage_moe_waves_run",
     "xstage_moe_waves_plan",
     "xstage_burst_gap_run",
@@ -272,6 +274,20 @@ def _m_ulysses_attn_fwd_kv_staged(q_src, k_src, v_src, workspace, out_dst, H_loc
     return _ulysses_ws_call(q_src, k_src, v_src, workspace, out_dst, H_local, h0, scale, split_ws, stream, 2)
 
 
+def _m_attn_a2a_fwd_nsplit(q, k, v, out_slabs, n_split, scale=None, split_ws=None, stream=None):
+    B, S, H, D = _qkv(q, k, v)
+    ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
+    arr, keep = ptr_array(ptrs)
+    need = xstage_attn_nsplit_ws_size(B, S, H, D, n_split)
+    if need and split_ws is None:
+        raise ValueError(f"n_split={n_split} needs a split workspace of {need} bytes (xstage_attn_nsplit_ws_size)")
+    ws, wsb = (None, 0) if split_ws is None else (_dev_tensor(split_ws, "split_ws", device=q.device, min_bytes=need,
+                                                              bf16=False).data_ptr(), split_ws.numel() * split_ws.element_size())
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), arr, B, S, H, D, P, _scale(scale, D), int(n_split), ws, wsb,
+            _stream_of(q, stream))
+    return call, (q, k, v, out_slabs, keep, split_ws), q.device
+
+
 def _m_attn_a2a_fwd_paced(q, k, v, out_slabs, chunks, scale=None, stream=None):
     B, S, H, D = _qkv(q, k, v)
     ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
@@ -297,6 +313,7 @@ _MARSHAL = {
     "xstage_attn_a2a_unfused": _m_attn_a2a_unfused,
     "xstage_attn_a2a_fwd_traced": _m_attn_a2a_fwd_traced,
     "xstage_attn_a2a_fwd_paced": _m_attn_a2a_fwd_paced,
+    "xstage_attn_a2a_fwd_nsplit": _m_attn_a2a_fwd_nsplit,
     "xstage_attn_a2a_fwd_strided": _m_attn_a2a_fwd_strided,
     "xstage_ulysses_attn_fwd": _m_ulysses_attn_fwd,
     "xstage_ulysses_attn_unfused": _m_ulysses_attn_unfused,
@@ -356,6 +373,20 @@ def xstage_attn_a2a_fwd_paced(q, k, v, out_slabs, chunks, scale=None, stream=Non
     over the next tile's first key-loop iterations; slabs as xstage_attn_a2a_fwd's without
     split workspace, bit for bit; see include/xstage.h."""
     _invoke("xstage_attn_a2a_fwd_paced", q, k, v, out_slabs, chunks, scale=scale, stream=stream)
+
+
+def xstage_attn_a2a_fwd_nsplit(q, k, v, out_slabs, n_split, scale=None, split_ws=None, stream=None) -> None:
+    """Fused call with exactly ``n_split`` key splits per tile; ``split_ws`` holds at least
+    xstage_attn_nsplit_ws_size bytes (zero-filled; None for n_split = 1); see include/xstage.h."""
+    _invoke("xstage_attn_a2a_fwd_nsplit", q, k, v, out_slabs, n_split, scale=scale, split_ws=split_ws, stream=stream)
+
+
+def xstage_attn_nsplit_ws_size(B: int, S: int, H_local: int, D: int, n_split: int) -> int:
+    """Split workspace bytes of xstage_attn_a2a_fwd_nsplit for this shape and split count."""
+    b = ctypes.c_ulonglong(0)
+    _check(lib().xstage_attn_nsplit_ws_size(int(B), int(S), int(H_local), int(D), int(n_split), ctypes.byref(b)),
+           "xstage_attn_nsplit_ws_size")
+    return b.value
 
 
 def xstage_attn_a2a_paced_plan(B: int, S: int, H_local: int, D: int):

@@ -94,6 +94,8 @@ SIGNATURES = {
     "xstage_attn_a2a_schedule": (_i, [_i, _i, _i, _i, _u64, _i] + [ctypes.POINTER(_i)] * 5),
     "xstage_attn_a2a_fwd_traced": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f, _i, _vp] + _WS + [_vp]),
     "xstage_attn_a2a_fwd_paced": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "xstage_attn_a2a_fwd_nsplit": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f, _i] + _WS + [_vp]),
+    "xstage_attn_nsplit_ws_size": (_i, [_i, _i, _i, _i, _i, ctypes.POINTER(_u64)]),
     "xstage_attn_a2a_paced_plan": (_i, [_i, _i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "xstage_moe_waves_run": (_i, [ctypes.POINTER(MoeParams), _vp]),
     "xstage_moe_waves_plan": (_i, [_i, ctypes.POINTER(_i), _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 4),

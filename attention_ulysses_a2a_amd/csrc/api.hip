@@ -359,6 +359,39 @@ int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void
                          static_cast<hipStream_t>(stream), 1 + mode, stamps);
 }
 
+int xstage_attn_nsplit_ws_size(int B, int S, int H_local, int D, int n_split, unsigned long long* bytes) {
+  if (bytes == nullptr) return XSTAGE_ERR_INVALID;
+  const int st = check_shape(B, S, H_local, D, 1);
+  if (st != XSTAGE_OK) return st;
+  bool ok = false;
+  const unsigned long long need = attn_ws_forced(B, S, H_local, D, n_split, &ok);
+  if (!ok) return XSTAGE_ERR_INVALID;
+  *bytes = need;
+  return XSTAGE_OK;
+}
+
+int xstage_attn_a2a_fwd_nsplit(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
+                               int H_local, int D, int P, float scale, int n_split, void* split_ws,
+                               unsigned long long split_ws_bytes, void* stream) {
+  int st = check_shape(B, S, H_local, D, P);
+  if (st != XSTAGE_OK) return st;
+  bool ok = false;
+  const unsigned long long need = attn_ws_forced(B, S, H_local, D, n_split, &ok);
+  if (!ok || (need > 0 && (split_ws == nullptr || split_ws_bytes < need))) return XSTAGE_ERR_INVALID;
+  // checked like the product call's workspace, over the bytes this split count uses
+  st = check_qkv(q, k, v, scale);
+  if (st != XSTAGE_OK) return st;
+  const unsigned long long tb = tensor_bytes(B, S, H_local, D);
+  const Range wr = need ? range_of(split_ws, need) : Range{0, 0};
+  Range others[4] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), wr};
+  st = check_split_ws(need ? split_ws : nullptr, wr, others, 3);
+  if (st != XSTAGE_OK) return st;
+  st = check_slabs(out_slabs, P, tb / (unsigned long long)P, others, 4);
+  if (st != XSTAGE_OK) return st;
+  return launch_attn_any(q, k, v, make_table(out_slabs, P), B, S, H_local, D, P, scale, need ? split_ws : nullptr,
+                         need, static_cast<hipStream_t>(stream), 0, nullptr, nullptr, 0, n_split);
+}
+
 int xstage_attn_a2a_fwd_paced(const void* q, const void* k, const void* v, void* const* out_slabs, int B, int S,
                               int H_local, int D, int P, float scale, int chunks, void* stream) {
   const int st = check_attn_slabs(q, k, v, out_slabs, B, S, H_local, D, P, scale, nullptr, 0, nullptr, 0);

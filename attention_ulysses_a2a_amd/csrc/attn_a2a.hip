@@ -784,6 +784,13 @@ static int paced_per_cu() {
 
 // Workgroups of a paced launch (each runs tiles i, i + n, i + 2n, ...); returns the tile count
 // and sets *n_wg (0 if the occupancy query failed).
+unsigned long long attn_ws_forced(int B, int S, int H, int D, int n_split, bool* ok) {
+  SplitPlan plan;
+  size_t used = 0;
+  *ok = plan_forced(B * H * ((S + 127) / 128), (S + 63) / 64, D, n_split, &plan, &used);
+  return *ok ? used : 0;
+}
+
 int attn_paced_workgroups(int B, int S, int H, int D, int* n_wg) {
   const int n_tiles = B * H * ((S + 127) / 128);
   const int per = D == 128 ? paced_per_cu<128>() : paced_per_cu<64>();
@@ -900,13 +907,19 @@ int attn_schedule(int B, int S, int H, int D, unsigned long long ws_bytes, int c
 
 int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H, int D,
                     int P, float scale, void* ws, unsigned long long ws_bytes, hipStream_t stream, int mode,
-                    unsigned long long* stamps, const Layout* layout, int pace_chunks) {
+                    unsigned long long* stamps, const Layout* layout, int pace_chunks, int force_split) {
   static const Layout kDefaultLayout;
   const Layout& lay = layout ? *layout : kDefaultLayout;
   const int n_tiles = B * H * ((S + 127) / 128);
   const int nkv = (S + 63) / 64;
   size_t used = 0;
-  SplitPlan plan = plan_with_workspace(n_tiles, nkv, D, ws ? ws_bytes : 0ull, &used);
+  SplitPlan plan;
+  if (force_split > 0) {
+    if (!plan_forced(n_tiles, nkv, D, force_split, &plan, &used) || (used > 0 && (!ws || ws_bytes < used)))
+      return XSTAGE_ERR_INVALID;
+  } else {
+    plan = plan_with_workspace(n_tiles, nkv, D, ws ? ws_bytes : 0ull, &used);
+  }
   if (plan.n_split > 1) {
     plan.counters = static_cast<uint32_t*>(ws);
     plan.partial = static_cast<char*>(ws) + kCounterAreaBytes;

@@ -44,6 +44,12 @@ constexpr size_t kCounterAreaBytes = (size_t)kSplitMaxTiles * 4;
 // plans whose partials fit `partial_capacity` bytes (0: no split).
 SplitPlan choose_split(int n_tiles, int nkv, int D, size_t partial_capacity);
 
+// Plan with exactly n_split key splits (1: none) and the workspace bytes it uses (0 for
+// n_split = 1).  False when n_split is outside 1..15, the shape has more than kSplitMaxTiles
+// tiles (n_split > 1), nkv 64-key blocks cannot form exactly n_split non-empty equal ranges,
+// or the partials exceed kSplitPartialCap.
+bool plan_forced(int n_tiles, int nkv, int D, int n_split, SplitPlan* plan, size_t* used);
+
 // Plan of a launch given `ws_bytes` of split workspace (ws_bytes = 0: no workspace): the
 // counters take kCounterAreaBytes, the partials at most the rest (and at most
 // kSplitPartialCap); more than kSplitMaxTiles tiles are never split.  Returns the workspace bytes the plan uses in *used (0 without split).

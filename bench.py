@@ -17,7 +17,8 @@ then the separate scatter kernel), attention alone (P=1), the full-head Ulysses 
 CPU oracle timed on a bounded sample of the same workload (``cpu_baseline``).  ``--bg``
 instead runs the Burst-Gap store sweep and prints one JSON line per point plus the fitted
 parameters; ``--cpu-oracle-configs`` times the oracle on every configuration; ``--paced`` times
-the paced persistent epilogue for every chunk count against the Burst-Gap model's choice.
+the paced persistent epilogue for every chunk count against the Burst-Gap model's choice;
+``--split-study`` every key-split count against the split-count model over a grid of shapes.
 """
 
 from __future__ import annotations
@@ -67,6 +68,9 @@ def parse():
                     help="fused-epilogue overhead and store spans against sequence length (one JSON line per S)")
     ap.add_argument("--profile-launches", type=int, default=0,
                     help="only issue this many fused launches of the workload (for counter collection)")
+    ap.add_argument("--split-study", action="store_true",
+                    help="every key-split count against the split-count model over a grid of shapes "
+                         "(one JSON line per shape)")
     ap.add_argument("--paced", action="store_true",
                     help="paced persistent epilogue: every chunk count against the product call and the "
                          "Burst-Gap model's choice (one JSON line per workload)")
@@ -425,6 +429,11 @@ def main():
         from attention_ulysses_a2a_amd.xstage_study import run_study
 
         run_study(torch, xs, emit=lambda line: print(line, flush=True))
+        return
+    if args.split_study:
+        from attention_ulysses_a2a_amd.split_study import run as run_split
+
+        run_split(torch, xs, settle_s=args.settle_s, emit=lambda line: print(line, flush=True))
         return
     if args.paced:
         from attention_ulysses_a2a_amd.paced_study import run as run_paced

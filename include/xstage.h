@@ -246,6 +246,31 @@ int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void
                                unsigned long long* stamps, void* split_ws,
                                unsigned long long split_ws_bytes, void* stream);
 
+/* Split-count override of the fused call, for tuning and for checking the split-count model
+ * (plumbing of this work decomposition; the pages describe the fused call, "Contributions",
+ * FlashAttention-A2A item, not its decomposition).  xstage_attn_a2a_fwd with the key range of
+ * every 128-row tile split into exactly n_split ranges (1: no split) instead of the count the
+ * library's model picks; the same decomposition otherwise (ranges sized to the workgroups'
+ * CU placement when every workgroup fits on the device at once, equal ranges of 64-key
+ * blocks otherwise), and the same result contract: with the model's own count the slabs
+ * equal xstage_attn_a2a_fwd's bit for bit.
+ *   n_split: 1..15, and ceil(S / 64) blocks must form exactly n_split non-empty equal
+ *            ranges; shapes with more than 4096 tiles take n_split = 1 only;
+ *   split_ws: at least xstage_attn_nsplit_ws_size bytes (NULL allowed for n_split = 1),
+ *            16-byte aligned, zeroed before its first use, caller-owned, as for
+ *            xstage_attn_a2a_fwd (every call leaves the counters at zero).
+ * XSTAGE_ERR_INVALID for an unavailable n_split or a too small workspace, otherwise the
+ * argument errors of xstage_attn_a2a_fwd.  Never synchronizes or allocates. */
+int xstage_attn_a2a_fwd_nsplit(const void* q, const void* k, const void* v, void* const* out_slabs,
+                               int B, int S, int H_local, int D, int P, float scale, int n_split,
+                               void* split_ws, unsigned long long split_ws_bytes, void* stream);
+
+/* Split workspace bytes xstage_attn_a2a_fwd_nsplit needs for this shape and n_split: 0 for
+ * n_split = 1, else 16 KiB of counters plus n_tiles * n_split partial records of
+ * 4 * (D / 16 + 1) * 1 KiB (at most 128 MiB of partials).  Host only; XSTAGE_ERR_INVALID when
+ * n_split is unavailable for the shape (see above). */
+int xstage_attn_nsplit_ws_size(int B, int S, int H_local, int D, int n_split, unsigned long long* bytes);
+
 /* Paced fused attention + all-to-all: the burst-shaping use of the Burst-Gap model
  * ("Significance": the model as a way to shape the communication bursts and hide their
  * issuer-side cost; "Methodology": a burst of V followed by a gap G of compute) applied to

@@ -47,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 24
+    assert len(names) == 26
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -119,6 +119,43 @@ def paced(L, chunks, q=Q, B=1, S=256, H=2, D=128, P=2, scale=0.125):
 ])
 def test_paced_rejects(L, kw, code):
     assert paced(L, **kw) == code
+
+
+def test_nsplit_ws_size_values(L):
+    import ctypes
+
+    b = ctypes.c_ulonglong(7)
+    # FLUX-1024 share: 108 tiles, 72 key blocks; records of 4 waves x 9 chunks x 64 lanes x 16 B
+    assert L.xstage_attn_nsplit_ws_size(1, 4608, 3, 128, 1, ctypes.byref(b)) == 0 and b.value == 0
+    for k in (2, 3, 4, 8, 9, 12):
+        assert L.xstage_attn_nsplit_ws_size(1, 4608, 3, 128, k, ctypes.byref(b)) == 0
+        assert b.value == 16384 + 108 * k * 4 * 9 * 64 * 16
+    # 16 and 0 are out of range; 5 blocks (S = 300) cannot form 4 equal non-empty ranges
+    # (2 blocks each gives 3 ranges), but they form 3
+    assert L.xstage_attn_nsplit_ws_size(1, 4608, 3, 128, 16, ctypes.byref(b)) == INVALID
+    assert L.xstage_attn_nsplit_ws_size(1, 4608, 3, 128, 0, ctypes.byref(b)) == INVALID
+    assert L.xstage_attn_nsplit_ws_size(1, 300, 1, 64, 4, ctypes.byref(b)) == INVALID
+    assert L.xstage_attn_nsplit_ws_size(1, 300, 1, 64, 3, ctypes.byref(b)) == 0
+    assert b.value == 16384 + 3 * 3 * 4 * 5 * 64 * 16
+    # more than 4096 tiles: only n_split = 1; partials above 128 MiB: refused
+    assert L.xstage_attn_nsplit_ws_size(1, 128 * 4097, 1, 64, 2, ctypes.byref(b)) == INVALID
+    assert L.xstage_attn_nsplit_ws_size(1, 16896, 3, 128, 15, ctypes.byref(b)) == INVALID
+    assert L.xstage_attn_nsplit_ws_size(1, 4608, 3, 128, 2, None) == INVALID
+
+
+@no_device
+def test_nsplit_rejects(L):
+    arr, keep = _lib.ptr_array(slabs(2))
+    call = lambda k, ws=WS, wsb=1 << 30, q=Q: L.xstage_attn_a2a_fwd_nsplit(q, K, V, arr, 1, 4608, 3, 128, 2, 0.1,
+                                                                         k, ws, wsb, None)
+    assert call(0) == INVALID
+    assert call(16) == INVALID
+    assert call(4, ws=None) == INVALID                    # split count needs a workspace
+    assert call(4, wsb=16384) == INVALID                  # too small
+    assert call(4, ws=WS + 8) == INVALID                  # misaligned
+    assert call(4, ws=Q) == INVALID                       # overlaps q
+    assert call(4, q=0) == INVALID
+    assert L.xstage_attn_a2a_fwd_nsplit(Q, K, V, arr, 1, 4608, 3, 96, 2, 0.1, 1, None, 0, None) == UNSUPPORTED
 
 
 @no_device
