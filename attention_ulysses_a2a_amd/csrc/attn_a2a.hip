@@ -284,16 +284,13 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
   // (kernel arguments, scalar loads) and the block offset is in the per-lane offset.
   const uint16_t* const kbase = SRC != kShards ? a.k + head0 : nullptr;
   const uint16_t* const vbase = SRC != kShards ? a.v + head0 : nullptr;
-  // Shard cursors (kShards): first row of the shard holding the K (V) stream's current block and
-  // that shard's resource; blocks only move forward, from j0.
-  int k_lo = 0, v_lo = 0;
-  __amdgpu_buffer_rsrc_t k_r, v_r;
-  if constexpr (SRC == kShards) {
-    const int p = j0 * C::BN / a.src_rows;
-    k_lo = v_lo = p * a.src_rows;
-    k_r = make_rsrc(uniform_ptr(src.k[p]));
-    v_r = make_rsrc(uniform_ptr(src.v[p]));
-  }
+  // Shard cursors (kShards): the shard holding the K (V) stream's current block; blocks only
+  // move forward, from j0.  The cursor is an index, and each load builds its buffer resource
+  // from the shard pointer read at that index made wave-uniform (readfirstlane): a resource
+  // carried across the loop as a value is not provably uniform to the compiler, which then
+  // wraps every copy in a loop over the lanes' resources.
+  int k_p = 0, v_p = 0;
+  if constexpr (SRC == kShards) k_p = v_p = j0 * C::BN / a.src_rows;
   // Byte offset of this lane's chunk from the block's first key, for its first load; load i
   // of the lane is RSTEP rows further on (the swizzle repeats every 16 rows, so the chunk
   // column is the same): one per-lane register, the rest is a wave-uniform offset.
@@ -321,10 +318,13 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
       // p0 .. p1, each lane from exactly one of them (every LDS chunk written once), and
       // moves the cursor to the shard of its last row.
       const bool is_k = slot_byte < 2 * C::BLKB;
-      int& cur_lo = is_k ? k_lo : v_lo;
-      __amdgpu_buffer_rsrc_t& cur_r = is_k ? k_r : v_r;
+      int& cur_p = is_k ? k_p : v_p;
+      const uint16_t* const* tbl = is_k ? src.k : src.v;
+      const int cp = __builtin_amdgcn_readfirstlane(cur_p);
+      const int cur_lo = cp * a.src_rows;
       const int last = min(n0 + C::BN, S) - 1;
       if (last < cur_lo + a.src_rows) {
+        const __amdgpu_buffer_rsrc_t cur_r = make_rsrc(uniform_ptr(tbl[cp]));
         const uint32_t boff = (uint32_t)(n0 - cur_lo) * rs * 2u;
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i)
@@ -332,10 +332,10 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
               cur_r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
               ld_voff + (i * ld_step + boff), 0, 0, 0);
       } else {
-        const uint16_t* const* tbl = is_k ? src.k : src.v;
-        const int p0 = n0 / a.src_rows, p1 = last / a.src_rows;
+        const int p0 = __builtin_amdgcn_readfirstlane(n0 / a.src_rows);
+        const int p1 = __builtin_amdgcn_readfirstlane(last / a.src_rows);
         for (int p = p0; p <= p1; ++p) {
-          const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(tbl[p]));
+          const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(tbl[__builtin_amdgcn_readfirstlane(p)]));
           const int lo = p * a.src_rows - n0;                        // first block row in shard p
           const int hi = p == p1 ? C::BN : (p + 1) * a.src_rows - n0;  // one past its last
           const uint32_t boff = (uint32_t)(n0 - p * a.src_rows) * rs * 2u;
@@ -348,8 +348,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
                   ld_voff + (i * ld_step + boff), 0, 0, 0);
           }
         }
-        cur_lo = p1 * a.src_rows;
-        cur_r = make_rsrc(uniform_ptr(tbl[p1]));
+        cur_p = p1;
       }
     }
   };

@@ -173,10 +173,10 @@ int xstage_ulysses_attn_unfused(const void* const* q_src, const void* const* k_s
  * into out_dst as xstage_ulysses_attn_fwd does, all on `stream`.  Every query tile reads
  * all of K and V, so at long sequences the gathered copies keep those reads to one
  * contiguous buffer each, while Q (read once) and the output (written once) keep the
- * fused all-to-all.  Measured on MI355X (H_local = H/8, D = 128): 6 to 9 % faster than
- * xstage_ulysses_attn_fwd once one tensor's shards span about 100 MB or more
- * (S * H * D * 2 bytes), slower at 28 MB, where the two extra launches cost more than the
- * in-place reads lose.  workspace: caller-owned, 2 * B * S * H_local * D * 2 bytes (k,
+ * fused all-to-all.  Measured on MI355X (H_local = H/8, D = 128): about 3 % faster than
+ * xstage_ulysses_attn_fwd when one tensor's shards span 335 MB (S * H * D * 2 bytes), level
+ * at about 100 MB, and 24 % slower at 28 MB, where the two extra launches cost more than
+ * the in-place reads lose.  workspace: caller-owned, 2 * B * S * H_local * D * 2 bytes (k,
  * then v), disjoint from every shard and output.  Requirements and result as for
  * xstage_ulysses_attn_fwd, bit for bit. */
 int xstage_ulysses_attn_fwd_kv_staged(const void* const* q_src, const void* const* k_src,
