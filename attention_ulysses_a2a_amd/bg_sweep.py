@@ -198,8 +198,9 @@ def run_sweep(torch, xs, out=print, variants=("hot", "cold")):
     return summary
 
 
-def summarize(lines):
-    """Markdown summary of a sweep's JSON lines (the output of ``bench.py --bg``)."""
+def summarize(lines, jsonl_path="bg_sweep.jsonl"):
+    """Markdown summary of a sweep's JSON lines (the output of ``bench.py --bg``, saved at
+    ``jsonl_path``)."""
     recs = [json.loads(ln) for ln in lines if ln.strip().startswith("{")]
     pts = [r["bg"] for r in recs if "bg" in r]
     fits = {r["bg_fit"]["variant"]: r["bg_fit"] for r in recs if "bg_fit" in r}
@@ -215,8 +216,8 @@ def summarize(lines):
     cp = next((r["bg_copy"] for r in recs if "bg_copy" in r), None)
     cal = next((r["bg_calibration"] for r in recs if "bg_calibration" in r), {})
     md = ["# Burst-Gap store sweep on one MI355X (xstage_burst_gap_run)", "",
-          "Command (repository root): `python bench.py --bg > gpurun_out/bg_sweep.jsonl`, then",
-          "`python -m attention_ulysses_a2a_amd.bg_sweep gpurun_out/bg_sweep.jsonl` writes this summary.", ""]
+          f"Command (repository root): `python bench.py --bg > {jsonl_path}`, then",
+          f"`python -m attention_ulysses_a2a_amd.bg_sweep {jsonl_path}` writes this summary.", ""]
     if cal:
         md.append(f"Wall clock {cal['wallclock_hz'] / 1e6:.0f} MHz; gap loop calibrated at "
                   f"{cal['gap_ns_per_fma_iter']:.2f} ns per dependent-FMA iteration.")
@@ -296,4 +297,4 @@ if __name__ == "__main__":
     import sys
 
     with open(sys.argv[1]) as fh:
-        sys.stdout.write(summarize(fh.readlines()))
+        sys.stdout.write(summarize(fh.readlines(), sys.argv[1]))

@@ -145,13 +145,14 @@ def run_study(torch, xs, S_list=DEFAULT_S, H=3, D=128, P=8, seed=11, target_s=0.
     return rows
 
 
-def summarize(lines, source_hash):
-    """Markdown table of a study's JSON lines (the output of ``bench.py --xstage-study``)."""
+def summarize(lines, source_hash, jsonl_path="xstage_study.jsonl"):
+    """Markdown table of a study's JSON lines (the output of ``bench.py --xstage-study``,
+    saved at ``jsonl_path``)."""
     rows = [json.loads(ln) for ln in lines if ln.strip().startswith("{")]
     md = ["# Fused-epilogue overhead and store spans against sequence length (one MI355X)", "",
           f"Kernel source hash (attn_a2a.hip + common.hpp, sha256 prefix): `{source_hash}`.", "",
-          "Command (repository root): `python3 bench.py --xstage-study > gpurun_out/xstage_study.jsonl`, then",
-          "`python -m attention_ulysses_a2a_amd.xstage_study gpurun_out/xstage_study.jsonl` writes this table",
+          f"Command (repository root): `python3 bench.py --xstage-study > {jsonl_path}`, then",
+          f"`python -m attention_ulysses_a2a_amd.xstage_study {jsonl_path}` writes this table",
           "(H_local=3, D=128, P=8, seeded N(0,1) inputs, inputs resident; after a 0.3 s settle phase, every",
           "call kind timed with HIP events over back-to-back launches in three interleaved rounds, medians).",
           "Times in µs per launch; loop clock in GHz.", "",
@@ -184,4 +185,4 @@ if __name__ == "__main__":
     import bench
 
     with open(sys.argv[1]) as fh:
-        sys.stdout.write(summarize(fh.readlines(), bench.kernel_source_hash()))
+        sys.stdout.write(summarize(fh.readlines(), bench.kernel_source_hash(), sys.argv[1]))
