@@ -7,11 +7,14 @@ sequence with the post-attention all-to-all written from the epilogue.  Inputs a
 synthetic bf16 tensors resident in HBM before the timed region.  Prints one JSON line.
 
 Every leg runs after one common settle phase (``--settle-s`` seconds of fused launches: the
-first launches of a process run up to ~6 % slow while the chip ramps up), then each leg gets
-the same ``--warmup`` untimed and ``--steps`` timed launches.  The headline is one block of
-exactly ``--steps`` fused launches between two synchronisations, timed with HIP events on the
-stream the kernel runs on.  Extra legs (reported inside the same line; the ratios come from
-three interleaved rounds of every leg): the serial path (attention into a contiguous buffer,
+first launches of a process run up to ~6 % slow while the chip ramps up).  The headline is
+one block of exactly ``--steps`` fused launches (after ``--warmup`` untimed ones) between two
+synchronisations, timed with HIP events on the stream the kernel runs on.  Extra legs
+(reported inside the same line) run in three interleaved rounds, every leg, the fused call
+included, with the same max(steps, 100) timed and max(warmup, 20) untimed launches per
+round (the clock shifts for about a millisecond when the kernel mix changes, so shorter
+windows measure the shift), and every ratio is taken between the legs' medians: the serial
+path (attention into a contiguous buffer,
 then the separate scatter kernel), attention alone (P=1), the full-head Ulysses layouts
 (strided destination; the whole layer reading its inputs from P sequence shards), and the
 CPU oracle timed on a bounded sample of the same workload (``cpu_baseline``).  ``--bg``
@@ -242,18 +245,18 @@ def bench_attention(args, torch, xs):
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / args.steps
 
-    # comparison legs: three interleaved rounds, every leg with the headline's warm-up and
-    # step count; the ratios are taken from the medians
+    # comparison legs: three interleaved rounds, every leg (the fused call included) with the
+    # same warm-up and step count; the ratios are taken between the medians
     import statistics
 
+    leg_steps, leg_warmup = max(args.steps, 100), max(args.warmup, 20)
     legs = {"fused": fused, "unfused": unfused, "attn": attn_only, "scatter": scatter_only}
     per = {n: [] for n in legs}
     for _ in range(3):
         for n, fn in legs.items():
-            per[n].append(timed(fn, args.steps, args.warmup, torch))
+            per[n].append(timed(fn, leg_steps, leg_warmup, torch))
     med = {n: statistics.median(v) for n, v in per.items()}
     ms_unfused, ms_attn, ms_scatter = med["unfused"], med["attn"], med["scatter"]
-    leg_warmup = args.warmup
 
     # Full-head Ulysses layouts, as rank 5 of a group of P ranks over H_local * P heads:
     # the strided epilogue (receive buffers [B, S/P, H, D], this rank's head columns) and the
@@ -277,7 +280,7 @@ def bench_attention(args, torch, xs):
     uper = {n: [] for n in ulegs}
     for _ in range(3):
         for n, fn in ulegs.items():
-            uper[n].append(timed(fn, args.steps, leg_warmup, torch))
+            uper[n].append(timed(fn, leg_steps, leg_warmup, torch))
     umed = {n: statistics.median(v) for n, v in uper.items()}
     ms_strided, ms_layer = umed["strided"], umed["layer"]
     ms_layer_serial, ms_layer_staged = umed["layer_serial"], umed["layer_staged"]
@@ -322,6 +325,8 @@ def bench_attention(args, torch, xs):
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "settle_s": round(args.settle_s, 3),
         "settle_launches": settle_n,
+        "leg_steps": leg_steps,
+        "leg_warmup": leg_warmup,
         "split_ws_bytes": 0 if sws is None else int(sws.numel()),
         "fused_vs_unfused": round(ms_unfused / med["fused"], 4),
         "fused_vs_attention_only": round(med["fused"] / ms_attn, 4),
