@@ -631,9 +631,9 @@ def bind(name: str, *args, **kwargs) -> _Bound:
     current stream of the tensors' device unless ``stream`` is given), and the calls must be
     made with that device current.  Supported: the attention entry points
     (xstage_attn_a2a_fwd, xstage_attn_fwd, xstage_a2a_scatter, xstage_attn_a2a_unfused,
-    xstage_attn_a2a_fwd_traced, xstage_attn_a2a_fwd_paced, xstage_attn_a2a_fwd_strided,
-    xstage_ulysses_attn_fwd, xstage_ulysses_attn_unfused, xstage_ulysses_attn_fwd_kv_staged,
-    xstage_attn_a2a_fwd_noalloc) and
+    xstage_attn_a2a_fwd_traced, xstage_attn_a2a_fwd_paced, xstage_attn_a2a_fwd_nsplit,
+    xstage_attn_a2a_fwd_strided, xstage_ulysses_attn_fwd, xstage_ulysses_attn_unfused,
+    xstage_ulysses_attn_fwd_kv_staged, xstage_attn_a2a_fwd_noalloc) and
     xstage_moe_waves_run, with the same arguments as the functions.
     """
     import torch
