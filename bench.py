@@ -304,7 +304,7 @@ def bench_attention(args, torch, xs):
 
     tflops = w.flops / (ms * 1e-3) / 1e12
     res = {
-        "metric": METRIC,
+        "metric": METRIC if w.S == 4608 else METRIC.replace("(S=4608,", f"(S={w.S},"),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
