@@ -46,6 +46,7 @@ __all__ = [
     "xstage_ulysses_attn_unfused",
     "xstage_ulysses_attn_fwd_kv_staged",
     "xstage_attn_a2a_plan",
+    "xstage_attn_a2a_wg_rows",
     "xstage_attn_a2a_schedule",
     "xstage_attn_a2a_fwd_traced",
     "xstage_attn_a2a_fwd_paced",
@@ -211,7 +212,8 @@ def _m_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, split_w
     ptrs, P = _slab_ptrs(out_slabs, q.device, _slab_need(B, S, H, D))
     ws, wsb = _split_ws(split_ws, q.device)
     nwg, _ = xstage_attn_a2a_plan(B, S, H, D, wsb)
-    _dev_tensor(stamps, "stamps", device=q.device, min_bytes=nwg * 16 * 8, bf16=False)
+    waves = xstage_attn_a2a_wg_rows(B, S, H, D, wsb) // 32
+    _dev_tensor(stamps, "stamps", device=q.device, min_bytes=nwg * waves * 4 * 8, bf16=False)
     if stamps.element_size() != 8:
         raise ValueError("stamps must be a 64-bit tensor")
     arr, keep = ptr_array(ptrs)
@@ -362,7 +364,8 @@ def xstage_attn_a2a_unfused(q, k, v, workspace, out_slabs, scale=None, split_ws=
 
 def xstage_attn_a2a_fwd_traced(q, k, v, out_slabs, mode, stamps, scale=None, split_ws=None, stream=None) -> None:
     """Instrumented fused call (store-span study); ``stamps`` is an int64 device tensor of
-    n_workgroups * 16 entries (xstage_attn_a2a_plan with the same workspace); modes as in
+    n_workgroups * waves * 4 entries, [workgroup][wave][4] (xstage_attn_a2a_plan and
+    xstage_attn_a2a_wg_rows with the same workspace: waves = rows // 32); modes as in
     include/xstage.h."""
     _invoke("xstage_attn_a2a_fwd_traced", q, k, v, out_slabs, mode, stamps, scale=scale, split_ws=split_ws,
             stream=stream)
@@ -492,9 +495,21 @@ def xstage_attn_a2a_plan(B: int, S: int, H_local: int, D: int, split_ws_bytes=No
     return nwg.value, nsp.value
 
 
+def xstage_attn_a2a_wg_rows(B: int, S: int, H_local: int, D: int, split_ws_bytes=None) -> int:
+    """Query rows per workgroup (128: 4 waves, or 256: 8 waves) of the attention launch for
+    this shape on the current device given ``split_ws_bytes`` of split workspace (None: as
+    much as the fastest plan uses)."""
+    rows = ctypes.c_int(0)
+    wsb = WS_FULL if split_ws_bytes is None else int(split_ws_bytes)
+    _check(lib().xstage_attn_a2a_wg_rows(int(B), int(S), int(H_local), int(D), wsb, ctypes.byref(rows)),
+           "xstage_attn_a2a_wg_rows")
+    return rows.value
+
+
 def xstage_attn_a2a_schedule(B: int, S: int, H_local: int, D: int, split_ws_bytes=None):
     """Per-workgroup (tile, split, j0, j1) of the attention launch for this shape on the
-    current device, as four lists (key blocks of 64 in [j0, j1))."""
+    current device, as four lists (tiles of xstage_attn_a2a_wg_rows query rows; key blocks
+    of 64 in [j0, j1))."""
     nwg, _ = xstage_attn_a2a_plan(B, S, H_local, D, split_ws_bytes)
     wsb = WS_FULL if split_ws_bytes is None else int(split_ws_bytes)
     arrs = [(ctypes.c_int * max(nwg, 1))() for _ in range(4)]

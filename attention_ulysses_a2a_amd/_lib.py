@@ -91,6 +91,7 @@ SIGNATURES = {
     "xstage_ulysses_attn_fwd_kv_staged": (
         _i, [_PP, _PP, _PP, _vp, _PP, _i, _i, _i, _i, _i, _i, _i, _f] + _WS + [_vp]),
     "xstage_attn_a2a_plan": (_i, [_i, _i, _i, _i, _u64, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "xstage_attn_a2a_wg_rows": (_i, [_i, _i, _i, _i, _u64, ctypes.POINTER(_i)]),
     "xstage_attn_a2a_schedule": (_i, [_i, _i, _i, _i, _u64, _i] + [ctypes.POINTER(_i)] * 5),
     "xstage_attn_a2a_fwd_traced": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f, _i, _vp] + _WS + [_vp]),
     "xstage_attn_a2a_fwd_paced": (_i, [_vp, _vp, _vp, _PP, _i, _i, _i, _i, _i, _f, _i, _vp]),

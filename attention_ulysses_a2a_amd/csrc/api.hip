@@ -330,6 +330,14 @@ int xstage_attn_a2a_plan(int B, int S, int H_local, int D, unsigned long long sp
   return XSTAGE_OK;
 }
 
+int xstage_attn_a2a_wg_rows(int B, int S, int H_local, int D, unsigned long long split_ws_bytes, int* rows) {
+  if (rows == nullptr) return XSTAGE_ERR_INVALID;
+  const int st = check_shape(B, S, H_local, D, 1);
+  if (st != XSTAGE_OK) return st;
+  *rows = attn_wg_rows(B, S, H_local, D, split_ws_bytes);
+  return XSTAGE_OK;
+}
+
 int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, unsigned long long split_ws_bytes, int cap, int* tile,
                              int* split, int* j0, int* j1, int* n_workgroups) {
   if (n_workgroups == nullptr || cap < 0 || (cap > 0 && (!tile || !split || !j0 || !j1))) return XSTAGE_ERR_INVALID;
@@ -346,8 +354,10 @@ int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void
     return XSTAGE_ERR_INVALID;
   int st = check_shape(B, S, H_local, D, P);
   if (st != XSTAGE_OK) return st;
-  const unsigned long long stamp_bytes =
-      (unsigned long long)attn_workgroups(B, S, H_local, D, split_ws ? split_ws_bytes : 0ull, nullptr) * 16ull * 8ull;
+  // [workgroup][wave][4] 64-bit stamps
+  const unsigned long long wsb = split_ws ? split_ws_bytes : 0ull;
+  const unsigned long long stamp_bytes = (unsigned long long)attn_workgroups(B, S, H_local, D, wsb, nullptr) *
+                                         (unsigned long long)(attn_wg_rows(B, S, H_local, D, wsb) / 32) * 4ull * 8ull;
   const Range sr = range_of(stamps, stamp_bytes);
   const unsigned long long tb = tensor_bytes(B, S, H_local, D);
   if (q && (overlaps(sr, range_of(q, tb)) || overlaps(sr, range_of(k, tb)) || overlaps(sr, range_of(v, tb))))

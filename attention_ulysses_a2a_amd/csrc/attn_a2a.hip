@@ -7,14 +7,17 @@
 // the stores time to drain; no wave is set aside for communication.  Here the P
 // destinations are P receive buffers ("slabs") in local HBM.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one (batch, head)):
+// Work decomposition (one workgroup = NW waves = 32 NW query rows of one (batch, head); NW = 4,
+// or 8 for launches that give every CU two 4-wave workgroups' worth of work without the
+// one-round unit table):
 //   * each wave owns 32 query rows and keeps them in registers as the B operand of
 //     v_mfma_f32_32x32x16_bf16; scores are computed transposed, S^T = K Q^T, so that one
 //     lane holds 32 keys of ONE query: the row max is a max over the lane's registers plus
 //     one swap of wave halves, and the row sum never leaves the lane until the end;
 //   * K and V blocks of 64 keys are staged in LDS (double-buffered, XOR-swizzled 16-byte
-//     chunks) by all 256 threads; the next block's global loads are in flight while the
-//     current block is computed;
+//     chunks) by all threads of the workgroup, and every wave reads them: 8 waves halve the
+//     copies per query row; the next block's global loads are in flight while the current
+//     block is computed;
 //   * O^T = V^T P^T: P^T comes straight out of the score accumulators (converted to bf16),
 //     and V^T operands are read from the natural [key][d] LDS layout with
 //     ds_read_b64_tr_b16, the gfx950 transposing LDS read;
@@ -32,11 +35,11 @@
 
 namespace xstage {
 
-template <int D>
+template <int D, int NW = 4>
 struct AttnCfg {
-  static constexpr int BM = 128;        // query rows per workgroup
-  static constexpr int BN = 64;         // keys per block
-  static constexpr int THREADS = 256;   // 4 waves of 64
+  static constexpr int BM = 32 * NW;     // query rows per workgroup
+  static constexpr int BN = 64;          // keys per block
+  static constexpr int THREADS = 64 * NW;  // NW waves of 64
   static constexpr int KS = D / 16;     // 16-wide k-steps of the score product
   static constexpr int DT = D / 32;     // 32-wide tiles of the output dimension
   static constexpr int CH = D / 8;      // 16-byte chunks per row
@@ -121,13 +124,16 @@ struct NoSrc {};
 // the shards, K and V from contiguous [B, S, H, D] tensors (a.k, a.v).
 enum SrcMode { kPlain = 0, kShards = 1, kShardQ = 2 };
 
-template <int D, int MODE, int SRC>
-__global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(const AttnArgs a, const UnitTable tab,
+// NW = 4: two workgroups per CU (two waves per SIMD); NW = 8: one workgroup per CU, also two
+// waves per SIMD; the paced mode holds 96 KiB of LDS, one 4-wave workgroup per CU.
+template <int D, int MODE, int SRC, int NW = 4>
+__global__ __launch_bounds__(64 * NW, (MODE == kPaced || NW == 8) ? 1 : 2) void attn_a2a_kernel(const AttnArgs a, const UnitTable tab,
                                                           const std::conditional_t<SRC != kPlain, SrcTable, NoSrc> src) {
   // The body names device-only types (the buffer resource), which the host pass of a
   // template cannot instantiate; the host pass only needs the launch signature.
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = AttnCfg<D>;
+  using C = AttnCfg<D, NW>;
+  static_assert(NW == 4 || (NW == 8 && MODE != kPaced), "4-wave workgroups, or 8 outside the paced mode");
   // K0 K1 V0 V1 as four LDS objects rather than one array: the compiler then knows that the
   // reads of one slot do not alias the asynchronous global->LDS copies into another, and
   // does not wait for those copies before every read.  Slots are named by the byte offsets
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
   constexpr bool kStamped = MODE == kTraced || MODE == kCoupled || MODE == kNoStore;
   // Paced mode: the finished tile's rows (4 waves x 32 rows, restaged as in the epilogue)
   // wait here while the next tile's key loop runs.
-  __shared__ __attribute__((aligned(16))) char lds_out[kPace ? 4 * 32 * C::ROWB : 16];
+  __shared__ __attribute__((aligned(16))) char lds_out[kPace ? NW * 32 * C::ROWB : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
   // stamp stays live across the key loop and the merge.
   auto stamp = [&](int slot, unsigned long long v) {
     if constexpr (kStamped) {
-      if (lane == 0) a.stamps[((size_t)blockIdx.x * 4 + w) * 4 + slot] = v;
+      if (lane == 0) a.stamps[((size_t)blockIdx.x * NW + w) * 4 + slot] = v;
     }
   };
   // Entries 2 and 3 start at 0: a workgroup that stores no output (a split that does not
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
   }
 
   // K/V blocks go from global memory straight into LDS (buffer_load_dwordx4 ... lds: no
-  // registers).  One instruction of wave w fills the 1 KiB LDS segment (i*4 + w) of a
+  // registers).  One instruction of wave w fills the 1 KiB LDS segment (i*NW + w) of a
   // block, lane by lane, so each lane fetches the global chunk that belongs at its LDS slot
   // under the swizzle.  The range check covers the per-lane offset (the scalar offset
   // stays 0), and a resource ends where the head's S rows end: rows past the end of the
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
   // Byte offset of this lane's chunk from the block's first key, for its first load; load i
   // of the lane is RSTEP rows further on (the swizzle repeats every 16 rows, so the chunk
   // column is the same): one per-lane register, the rest is a wave-uniform offset.
-  constexpr int RSTEP = 4 * 64 / C::CH;
+  constexpr int RSTEP = NW * 64 / C::CH;
   static_assert(RSTEP % 16 == 0, "the swizzle must repeat between a lane's loads");
   const int ld_row = (w * 64 + lane) / C::CH;
   const uint32_t ld_voff = ((uint32_t)ld_row * rs + (uint32_t)((((w * 64 + lane) % C::CH) ^ swz<D>(ld_row)) * 8)) * 2u;
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
 #pragma unroll
       for (int i = 0; i < C::NLD; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
+            rsrc, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * NW + wu) * 1024), 16,
             ld_voff + i * ld_step, 0, 0, 0);
     } else {
       // The stream's cursor (K or V: which one is fixed by the slot, a constant after
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
 #pragma unroll
         for (int i = 0; i < C::NLD; ++i)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              cur_r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
+              cur_r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * NW + wu) * 1024), 16,
               ld_voff + (i * ld_step + boff), 0, 0, 0);
       } else {
         const int p0 = __builtin_amdgcn_readfirstlane(n0 / a.src_rows);
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
             const int row = ld_row + i * RSTEP;
             if (row >= lo && row < hi)
               __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                  r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * 4 + wu) * 1024), 16,
+                  r, (__attribute__((address_space(3))) void*)(sp(slot_byte) + (i * NW + wu) * 1024), 16,
                   ld_voff + (i * ld_step + boff), 0, 0, 0);
           }
         }
@@ -575,7 +581,7 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
     // count, the count before the last arriver's loads; no cache write-back or invalidate.
     constexpr int kDeviceScope = 16;  // cache policy bits: sc1
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(a.partial, (short)0, a.partial_bytes, 0x00020000);
-    auto rec = [&](int sp) { return (((uint32_t)(tile * a.n_split + sp) * 4u + (uint32_t)w) * PREC * 64u + (uint32_t)lane) * 16u; };
+    auto rec = [&](int sp) { return (((uint32_t)(tile * a.n_split + sp) * (uint32_t)NW + (uint32_t)w) * PREC * 64u + (uint32_t)lane) * 16u; };
     u32x4 own[OCH];  // this split's record, kept for the merge should it arrive last
     {
       const uint32_t r = rec(split);
@@ -666,10 +672,14 @@ __global__ __launch_bounds__(256, MODE == kPaced ? 1 : 2) void attn_a2a_kernel(c
 
   // ---- epilogue: normalise, bf16, restage per wave, store rows into their slabs ----------
   const float inv = 1.0f / sum_with_partner32(l_run);
-  // wave-private [32][D] restage area in the K slots (free after the loop); paced mode: in
-  // lds_out, once the previous tile's rows have all been issued from there
+  // wave-private [32][D] restage area: 4 waves use the K slots (no wave reads them after the
+  // loop's last barrier); 8 waves need the V slots too, which the other waves may still be
+  // reading in the last block's PV product until this barrier; paced mode: in lds_out, once
+  // the previous tile's rows have all been issued from there
   if constexpr (kPace) issue_pending(a.pace_chunks);
-  char* stage = kPace ? lds_out + w * 32 * C::ROWB : (w < 2 ? lds_k0 : lds_k1) + (w & 1) * 32 * C::ROWB;
+  if constexpr (NW > 4) __syncthreads();
+  char* stage = kPace ? lds_out + w * 32 * C::ROWB
+                      : (NW > 4 ? sp((w >> 1) * C::BLKB) : (w < 2 ? lds_k0 : lds_k1)) + (w & 1) * 32 * C::ROWB;
   {
     const int n = lane & 31;
     const int sw = swz<D>(n);
@@ -781,8 +791,52 @@ static int paced_per_cu() {
   return n;
 }
 
-// Workgroups of a paced launch (each runs tiles i, i + n, i + 2n, ...); returns the tile count
-// and sets *n_wg (0 if the occupancy query failed).
+// One launch: the key-split plan (counted in 128-row tiles, as the split cost model and the
+// workspace layout count them) and the workgroup width.
+struct AttnLaunch {
+  SplitPlan plan;
+  int nw = 4;       // waves per workgroup; query rows per workgroup = 32 nw
+  int n_tiles = 0;  // (b, h, 32nw-row tile) units
+  int n_units = 0;  // workgroups = n_tiles * n_split
+  size_t used = 0;  // split workspace bytes the plan uses
+};
+
+// Width rule.  Eight waves over 256 query rows share every K/V block copied into LDS (half the
+// copies per query row of four waves over 128 rows), which measured 2-6 % faster per launch
+// on MI355X at the same split ranges, but a CU then holds one workgroup instead of two.  They
+// are used when the 4-wave launch keeps every CU at two workgroups without the one-round unit
+// table (no split and at least two workgroups per CU, or more workgroups than fit at once), and
+// every (b, h) has an even number of 128-row tiles: the 256-row tiles then cover the same rows
+// with the same key ranges and merge order (results bit for bit those of 4 waves) and the
+// split records take the same workspace bytes.
+static bool wide_launch(int S, int n_tiles4, int n_split, int cus) {
+  const long units4 = (long)n_tiles4 * n_split;
+  return ((S + 127) / 128) % 2 == 0 && units4 >= 2L * cus && (n_split == 1 || units4 > 2L * cus);
+}
+
+// force_split > 0: exactly that many splits (false if impossible or the workspace is too
+// small); otherwise the model's plan for ws_bytes of workspace.
+static bool attn_launch(int B, int S, int H, int D, unsigned long long ws_bytes, int force_split, bool allow_wide,
+                        AttnLaunch* L) {
+  const int n_tiles4 = B * H * ((S + 127) / 128);
+  const int nkv = (S + 63) / 64;
+  if (force_split > 0) {
+    if (!plan_forced(n_tiles4, nkv, D, force_split, &L->plan, &L->used)) return false;
+    if (L->used > 0 && ws_bytes < L->used) return false;
+  } else {
+    L->plan = plan_with_workspace(n_tiles4, nkv, D, ws_bytes, &L->used);
+  }
+  L->nw = allow_wide && wide_launch(S, n_tiles4, L->plan.n_split, cu_count()) ? 8 : 4;
+  L->n_tiles = L->nw == 8 ? n_tiles4 / 2 : n_tiles4;
+  L->n_units = L->n_tiles * L->plan.n_split;
+  return true;
+}
+
+// The one-round unit table (4-wave launches only; nullptr when out of its scope).
+static const UnitTable* launch_table(const AttnLaunch& L, int S) {
+  return L.nw == 4 && L.plan.n_split > 1 ? unit_table(L.n_tiles, (S + 63) / 64, L.plan.n_split) : nullptr;
+}
+
 unsigned long long attn_ws_forced(int B, int S, int H, int D, int n_split, bool* ok) {
   SplitPlan plan;
   size_t used = 0;
@@ -790,6 +844,8 @@ unsigned long long attn_ws_forced(int B, int S, int H, int D, int n_split, bool*
   return *ok ? used : 0;
 }
 
+// Workgroups of a paced launch (each runs tiles i, i + n, i + 2n, ...); returns the tile count
+// and sets *n_wg (0 if the occupancy query failed).
 int attn_paced_workgroups(int B, int S, int H, int D, int* n_wg) {
   const int n_tiles = B * H * ((S + 127) / 128);
   const int per = D == 128 ? paced_per_cu<128>() : paced_per_cu<64>();
@@ -797,10 +853,12 @@ int attn_paced_workgroups(int B, int S, int H, int D, int* n_wg) {
   return n_tiles;
 }
 
-template <int D>
+template <int D, int NW>
 static int launch_attn(const void* q, const void* k, const void* v, const SlabTable& slabs, int B, int S, int H,
-                       int P, float scale, const SplitPlan& plan, int mode, unsigned long long* stamps,
+                       int P, float scale, const AttnLaunch& L, int mode, unsigned long long* stamps,
                        const Layout& lay, int pace_chunks, hipStream_t stream) {
+  using C = AttnCfg<D, NW>;
+  const SplitPlan& plan = L.plan;
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -810,14 +868,14 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.S = S;
   a.H = H;
   a.S_P = S / P;
-  a.n_mtiles = (S + AttnCfg<D>::BM - 1) / AttnCfg<D>::BM;
+  a.n_mtiles = (S + C::BM - 1) / C::BM;
   a.n_split = plan.n_split;
   a.kvb_per_split = plan.kvb_per_split;
-  a.n_units = B * H * a.n_mtiles * plan.n_split;
+  a.n_units = L.n_units;
   a.c = fabsf(scale) * kLog2e;
   a.qflip = std::signbit(scale) ? 0x80008000u : 0u;
   a.partial = plan.partial;
-  a.partial_bytes = (int)((size_t)a.n_units * partial_bytes_per_unit(D));
+  a.partial_bytes = (int)((size_t)a.n_units * (NW / 4) * partial_bytes_per_unit(D));
   a.counters = plan.counters;
   a.pace_chunks = pace_chunks;
   a.stamps = stamps;
@@ -829,62 +887,69 @@ static int launch_attn(const void* q, const void* k, const void* v, const SlabTa
   a.dst_hs = lay.dst_heads > 0 ? lay.dst_heads : H;
   a.dst_h0 = lay.dst_head0;
   static const UnitTable kNoTable = {};
-  const UnitTable* tab = plan.n_split > 1 ? unit_table(a.n_units / plan.n_split, (S + 63) / 64, plan.n_split) : nullptr;
+  const UnitTable* tab = launch_table(L, S);
   a.use_table = tab != nullptr;
   const UnitTable& t = tab ? *tab : kNoTable;
-  const dim3 grid(a.n_units), block(AttnCfg<D>::THREADS);
+  const dim3 grid(a.n_units), block(C::THREADS);
   const NoSrc none;
-  if (mode == kPaced) {  // persistent: as many workgroups as fit at once, each runs several tiles
-    if (lay.src || plan.n_split != 1) return XSTAGE_ERR_INVALID;
-    const int n = paced_per_cu<D>();
-    if (n < 1) return XSTAGE_ERR_HIP;
-    const dim3 pgrid(std::min(a.n_units, cu_count() * n));
-    hipLaunchKernelGGL((attn_a2a_kernel<D, kPaced, kPlain>), pgrid, block, 0, stream, a, t, none);
-    return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
+  if constexpr (NW == 4) {
+    if (mode == kPaced) {  // persistent: as many workgroups as fit at once, each runs several tiles
+      if (lay.src || plan.n_split != 1) return XSTAGE_ERR_INVALID;
+      const int n = paced_per_cu<D>();
+      if (n < 1) return XSTAGE_ERR_HIP;
+      const dim3 pgrid(std::min(a.n_units, cu_count() * n));
+      hipLaunchKernelGGL((attn_a2a_kernel<D, kPaced, kPlain>), pgrid, block, 0, stream, a, t, none);
+      return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
+    }
+  } else {
+    if (mode == kPaced) return XSTAGE_ERR_INVALID;
   }
   if (lay.src) {  // shards: product mode only
     if (mode != kRun) return XSTAGE_ERR_INVALID;
     if (lay.kv_contiguous)
-      hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kShardQ>), grid, block, 0, stream, a, t, *lay.src);
+      hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kShardQ, NW>), grid, block, 0, stream, a, t, *lay.src);
     else
-      hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kShards>), grid, block, 0, stream, a, t, *lay.src);
+      hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kShards, NW>), grid, block, 0, stream, a, t, *lay.src);
   } else {
     switch (mode) {
-      case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced, kPlain>), grid, block, 0, stream, a, t, none); break;
-      case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled, kPlain>), grid, block, 0, stream, a, t, none); break;
-      case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore, kPlain>), grid, block, 0, stream, a, t, none); break;
-      default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kPlain>), grid, block, 0, stream, a, t, none); break;
+      case kTraced: hipLaunchKernelGGL((attn_a2a_kernel<D, kTraced, kPlain, NW>), grid, block, 0, stream, a, t, none); break;
+      case kCoupled: hipLaunchKernelGGL((attn_a2a_kernel<D, kCoupled, kPlain, NW>), grid, block, 0, stream, a, t, none); break;
+      case kNoStore: hipLaunchKernelGGL((attn_a2a_kernel<D, kNoStore, kPlain, NW>), grid, block, 0, stream, a, t, none); break;
+      default: hipLaunchKernelGGL((attn_a2a_kernel<D, kRun, kPlain, NW>), grid, block, 0, stream, a, t, none); break;
     }
   }
   return hipGetLastError() == hipSuccess ? XSTAGE_OK : XSTAGE_ERR_HIP;
 }
 
 int attn_workgroups(int B, int S, int H, int D, unsigned long long ws_bytes, int* n_split) {
-  const int n_tiles = B * H * ((S + 127) / 128);
-  size_t used = 0;
-  const SplitPlan plan = plan_with_workspace(n_tiles, (S + 63) / 64, D, ws_bytes, &used);
-  if (n_split) *n_split = plan.n_split;
-  return n_tiles * plan.n_split;
+  AttnLaunch L;
+  attn_launch(B, S, H, D, ws_bytes, 0, true, &L);
+  if (n_split) *n_split = L.plan.n_split;
+  return L.n_units;
+}
+
+int attn_wg_rows(int B, int S, int H, int D, unsigned long long ws_bytes) {
+  AttnLaunch L;
+  attn_launch(B, S, H, D, ws_bytes, 0, true, &L);
+  return 32 * L.nw;
 }
 
 // Workspace bytes a launch of this shape uses given ws_bytes of workspace (0: no split);
 // ws_bytes = ~0 gives the bytes of the unconstrained plan.
 unsigned long long attn_ws_used(int B, int S, int H, int D, unsigned long long ws_bytes) {
-  const int n_tiles = B * H * ((S + 127) / 128);
-  size_t used = 0;
-  plan_with_workspace(n_tiles, (S + 63) / 64, D, ws_bytes, &used);
-  return used;
+  AttnLaunch L;
+  attn_launch(B, S, H, D, ws_bytes, 0, true, &L);
+  return L.used;
 }
 
 int attn_schedule(int B, int S, int H, int D, unsigned long long ws_bytes, int cap, int* tile, int* split, int* j0,
                   int* j1) {
-  const int n_tiles = B * H * ((S + 127) / 128);
-  const int nkv = (S + 63) / 64;
-  size_t used = 0;
-  const SplitPlan plan = plan_with_workspace(n_tiles, nkv, D, ws_bytes, &used);
-  const int n = n_tiles * plan.n_split;
+  AttnLaunch L;
+  attn_launch(B, S, H, D, ws_bytes, 0, true, &L);
+  const int n = L.n_units;
   if (n > cap) return n;
-  const UnitTable* tab = plan.n_split > 1 ? unit_table(n_tiles, nkv, plan.n_split) : nullptr;
+  const int nkv = (S + 63) / 64;
+  const UnitTable* tab = launch_table(L, S);
   for (int i = 0; i < n; ++i) {
     if (tab) {
       const uint32_t e = tab->e[i];
@@ -894,11 +959,11 @@ int attn_schedule(int B, int S, int H, int D, unsigned long long ws_bytes, int c
       j1[i] = e >> 23;
     } else {  // the kernel's XCD-contiguous order with uniform splits
       const int q8 = n / 8, r8 = n % 8, x = i % 8, slot = i / 8;
-      const int L = x < r8 ? x * (q8 + 1) + slot : r8 * (q8 + 1) + (x - r8) * q8 + slot;
-      tile[i] = L / plan.n_split;
-      split[i] = L % plan.n_split;
-      j0[i] = split[i] * plan.kvb_per_split;
-      j1[i] = std::min(j0[i] + plan.kvb_per_split, nkv);
+      const int Lx = x < r8 ? x * (q8 + 1) + slot : r8 * (q8 + 1) + (x - r8) * q8 + slot;
+      tile[i] = Lx / L.plan.n_split;
+      split[i] = Lx % L.plan.n_split;
+      j0[i] = split[i] * L.plan.kvb_per_split;
+      j1[i] = std::min(j0[i] + L.plan.kvb_per_split, nkv);
     }
   }
   return n;
@@ -909,22 +974,17 @@ int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable
                     unsigned long long* stamps, const Layout* layout, int pace_chunks, int force_split) {
   static const Layout kDefaultLayout;
   const Layout& lay = layout ? *layout : kDefaultLayout;
-  const int n_tiles = B * H * ((S + 127) / 128);
-  const int nkv = (S + 63) / 64;
-  size_t used = 0;
-  SplitPlan plan;
-  if (force_split > 0) {
-    if (!plan_forced(n_tiles, nkv, D, force_split, &plan, &used) || (used > 0 && (!ws || ws_bytes < used)))
-      return XSTAGE_ERR_INVALID;
-  } else {
-    plan = plan_with_workspace(n_tiles, nkv, D, ws ? ws_bytes : 0ull, &used);
+  AttnLaunch L;
+  if (!attn_launch(B, S, H, D, ws ? ws_bytes : 0ull, force_split, mode != kPaced, &L)) return XSTAGE_ERR_INVALID;
+  if (L.plan.n_split > 1) {
+    L.plan.counters = static_cast<uint32_t*>(ws);
+    L.plan.partial = static_cast<char*>(ws) + kCounterAreaBytes;
   }
-  if (plan.n_split > 1) {
-    plan.counters = static_cast<uint32_t*>(ws);
-    plan.partial = static_cast<char*>(ws) + kCounterAreaBytes;
-  }
-  if (D == 128) return launch_attn<128>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, pace_chunks, stream);
-  return launch_attn<64>(q, k, v, slabs, B, S, H, P, scale, plan, mode, stamps, lay, pace_chunks, stream);
+  if (D == 128)
+    return L.nw == 8 ? launch_attn<128, 8>(q, k, v, slabs, B, S, H, P, scale, L, mode, stamps, lay, pace_chunks, stream)
+                     : launch_attn<128, 4>(q, k, v, slabs, B, S, H, P, scale, L, mode, stamps, lay, pace_chunks, stream);
+  return L.nw == 8 ? launch_attn<64, 8>(q, k, v, slabs, B, S, H, P, scale, L, mode, stamps, lay, pace_chunks, stream)
+                   : launch_attn<64, 4>(q, k, v, slabs, B, S, H, P, scale, L, mode, stamps, lay, pace_chunks, stream);
 }
 
 }  // namespace xstage

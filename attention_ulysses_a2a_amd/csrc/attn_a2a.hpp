@@ -20,6 +20,8 @@ int launch_attn_any(const void* q, const void* k, const void* v, const SlabTable
                     int force_split = 0);
 // Workgroups of a product launch given ws_bytes of split workspace; *n_split may be NULL.
 int attn_workgroups(int B, int S, int H, int D, unsigned long long ws_bytes, int* n_split);
+// Query rows per workgroup of that launch: 128 (4 waves) or 256 (8 waves).
+int attn_wg_rows(int B, int S, int H, int D, unsigned long long ws_bytes);
 // Workgroups of a paced launch in *n_wg (0 if the occupancy query failed); returns the tiles.
 int attn_paced_workgroups(int B, int S, int H, int D, int* n_wg);
 // Split-workspace bytes of a launch forced to n_split key splits (force_split above); *ok
@@ -27,7 +29,8 @@ int attn_paced_workgroups(int B, int S, int H, int D, int* n_wg);
 unsigned long long attn_ws_forced(int B, int S, int H, int D, int n_split, bool* ok);
 // Split-workspace bytes a launch of this shape uses given ws_bytes (~0: the full plan's).
 unsigned long long attn_ws_used(int B, int S, int H, int D, unsigned long long ws_bytes);
-// Per-workgroup (tile, split, j0, j1) of a product launch; returns the workgroup count.
+// Per-workgroup (tile, split, j0, j1) of a product launch (tiles of attn_wg_rows query rows);
+// returns the workgroup count.
 int attn_schedule(int B, int S, int H, int D, unsigned long long ws_bytes, int cap, int* tile, int* split, int* j0,
                   int* j1);
 

@@ -37,7 +37,7 @@ def coupled_prediction(t_fused_s: float, rounds: float, drain_s: float) -> float
 
 
 def spans_from_stamps(stamps: np.ndarray, hz: float):
-    """stamps: [n_workgroups, 4 waves, 4] ticks -> (epilogue spans, drain spans) in seconds,
+    """stamps: [n_workgroups, waves, 4] ticks -> (epilogue spans, drain spans) in seconds,
     over the waves that stored output."""
     st = stamps.reshape(-1, 4).astype(np.int64)
     emit = st[:, 2] > 0
@@ -92,7 +92,8 @@ def run_study(torch, xs, S_list=DEFAULT_S, H=3, D=128, P=8, seed=11, target_s=0.
         sl = [slabs[p] for p in range(P)]
         out1 = torch.empty((1, S, H, D), dtype=torch.bfloat16, device="cuda")
         nwg, nsp = xs.xstage_attn_a2a_plan(1, S, H, D)
-        stamps = [torch.zeros(nwg * 16, dtype=torch.int64, device="cuda") for _ in range(4)]
+        wg_rows = xs.xstage_attn_a2a_wg_rows(1, S, H, D)
+        stamps = [torch.zeros(nwg * (wg_rows // 32) * 4, dtype=torch.int64, device="cuda") for _ in range(4)]
         sws = xs.split_workspace(1, S, H, D)
         calls = {
             "attn": xs.bind("xstage_attn_fwd", q, k, v, out1, w.scale, split_ws=sws),
@@ -121,10 +122,10 @@ def run_study(torch, xs, S_list=DEFAULT_S, H=3, D=128, P=8, seed=11, target_s=0.
         epi, _ = spans_from_stamps(stamps[0].cpu().numpy(), hz)
         _, drain = spans_from_stamps(stamps[1].cpu().numpy(), hz)
         ghz = loop_clock_ghz(stamps[3].cpu().numpy(), hz)
-        rounds = nwg / slots
+        rounds = nwg * (wg_rows // 128) / slots  # slots: 128-row (4-wave) workgroups at once
         drain_med = float(np.median(drain)) if len(drain) else 0.0
         row = {
-            "S": S, "H_local": H, "D": D, "P": P, "workgroups": nwg, "key_splits": nsp, "rounds": round(rounds, 3),
+            "S": S, "H_local": H, "D": D, "P": P, "workgroups": nwg, "wg_rows": wg_rows, "key_splits": nsp, "rounds": round(rounds, 3),
             "t_attn_us": t["attn"] * 1e6, "t_fused_us": t["fused"] * 1e6, "t_traced_us": t["traced"] * 1e6,
             "t_nostore_us": t["nostore"] * 1e6, "t_coupled_us": t["coupled"] * 1e6,
             "overhead_fused_vs_attn_us": (t["fused"] - t["attn"]) * 1e6,
@@ -168,7 +169,8 @@ def summarize(lines, source_hash, jsonl_path="xstage_study.jsonl"):
           "coupled model | loop clock GHz |",
           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        md.append(f"| {r['S']} | {r['workgroups']} | {r['key_splits']} | {r['rounds']:.2f} | {r['t_attn_us']:.1f} | "
+        wg = f"{r['workgroups']}" + (f" × {r['wg_rows']} rows" if r.get("wg_rows", 128) != 128 else "")
+        md.append(f"| {r['S']} | {wg} | {r['key_splits']} | {r['rounds']:.2f} | {r['t_attn_us']:.1f} | "
                   f"{r['t_fused_us']:.1f} | {r['overhead_fused_vs_attn_us']:+.2f} | {r['t_traced_us']:.1f} | "
                   f"{r['t_nostore_us']:.1f} | {r['t_coupled_us']:.1f} | "
                   f"{r['t_traced_us'] - r['t_nostore_us']:+.2f} | {r['overhead_coupled_vs_nostore_us']:+.2f} | "

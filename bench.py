@@ -290,15 +290,16 @@ def bench_attention(args, torch, xs):
     # wall-clock ticks per wave), right after back-to-back fused launches: the published
     # peak assumes 2.4 GHz, while a chip running dense MFMA work clocks lower.
     nwg, _ = xs.xstage_attn_a2a_plan(w.B, w.S, w.H, w.D)
-    stamps = torch.zeros(nwg * 16, dtype=torch.int64, device="cuda")
+    waves = xs.xstage_attn_a2a_wg_rows(w.B, w.S, w.H, w.D) // 32
+    stamps = torch.zeros(nwg * waves * 4, dtype=torch.int64, device="cuda")
     clocked = xs.bind("xstage_attn_a2a_fwd_traced", q, k, v, slab_list, 3, stamps, w.scale, split_ws=sws)
     for _ in range(args.warmup):
         fused()
     clocked()
     torch.cuda.synchronize()
-    st = stamps.cpu().numpy().reshape(nwg, 4, 4).astype(np.int64)
-    wall = (st[:, :, 1] - st[:, :, 0]) / xs.xstage_wallclock_hz()
-    ticks = st[:, :, 3] - st[:, :, 2]
+    st = stamps.cpu().numpy().reshape(nwg * waves, 4).astype(np.int64)
+    wall = (st[:, 1] - st[:, 0]) / xs.xstage_wallclock_hz()
+    ticks = st[:, 3] - st[:, 2]
     use = wall > 2e-6
     loop_ghz = float(np.median(ticks[use] / wall[use]) / 1e9) if use.any() else None
 

@@ -201,17 +201,29 @@ int xstage_attn_a2a_unfused(const void* q, const void* k, const void* v, void* w
                             void* stream);
 
 /* Work decomposition of the attention entry points for this shape on the current device,
- * given split_ws_bytes of split workspace (0: none): *n_workgroups workgroups of 4 waves
- * (n_tiles x key splits, n_tiles = B * H_local * ceil(S / 128)), *n_split key splits per
- * 128-row tile (n_split may be NULL).  Host only; sizes the stamps of
- * xstage_attn_a2a_fwd_traced. */
+ * given split_ws_bytes of split workspace (0: none): *n_workgroups workgroups (n_tiles x key
+ * splits, n_tiles = B * H_local * ceil(S / rows), rows from xstage_attn_a2a_wg_rows), *n_split
+ * key splits per tile (n_split may be NULL).  The split count is chosen per 128-row tile; a
+ * launch of 256-row workgroups splits each of them the same way.  Host only; with
+ * xstage_attn_a2a_wg_rows it sizes the stamps of xstage_attn_a2a_fwd_traced. */
 int xstage_attn_a2a_plan(int B, int S, int H_local, int D, unsigned long long split_ws_bytes,
                          int* n_workgroups, int* n_split);
+
+/* Query rows per workgroup of that launch (*rows): 128 (4 waves of 32 rows) or 256 (8 waves;
+ * every K/V block staged in LDS then serves twice the rows).  256 is used when the launch with
+ * 128 gives every CU two workgroups without placement-sized key ranges (no split and at least
+ * two workgroups per CU, or more workgroups than fit at once) and every (b, h) has an even
+ * number of 128-row tiles; the key ranges and merge order per query row are then the same,
+ * and so is the result, bit for bit.  Plumbing of this work decomposition (the pages fix no
+ * tile shape; "Contributions", FlashAttention-A2A item, defines the fused call).  Host only. */
+int xstage_attn_a2a_wg_rows(int B, int S, int H_local, int D, unsigned long long split_ws_bytes,
+                            int* rows);
 
 /* The work decomposition xstage_attn_a2a_fwd uses for this shape on the current device
  * (256 CUs assumed when no device is present), given split_ws_bytes of split workspace:
  * for each of the *n_workgroups workgroups,
- * the tile it computes (index over (b, h, 128-row m-tile), m-tile fastest), its split
+ * the tile it computes (index over (b, h, m-tile of xstage_attn_a2a_wg_rows rows), m-tile
+ * fastest), its split
  * index within the tile (the merge order) and its half-open range [j0, j1) of 64-key
  * blocks.  The ranges of a tile's splits partition [0, ceil(S / 64)) in split order.
  * Launches whose workgroups fit on the device at once (more than one per CU) use ranges
@@ -234,8 +246,9 @@ int xstage_attn_a2a_schedule(int B, int S, int H_local, int D, unsigned long lon
  *   mode 3: as mode 0, but stamp entries [2] and [3] hold the shader-clock counter
  *           (s_memtime) at start and at the end of the key loop, so that
  *           ([3] - [2]) / ([1] - [0]) * xstage_wallclock_hz is the core clock the loop ran at;
- *   stamps: device uint64 [n_workgroups][4 waves][4] (xstage_attn_a2a_plan with the same
- *           split_ws_bytes, or 0 when split_ws is NULL), caller-owned,
+ *   stamps: device uint64 [n_workgroups][rows / 32 waves][4] (xstage_attn_a2a_plan and
+ *           xstage_attn_a2a_wg_rows with the same split_ws_bytes, or 0 when split_ws is
+ *           NULL), caller-owned,
  *           8-byte aligned, disjoint from every other argument; per wave, in wall-clock
  *           ticks (xstage_wallclock_hz): start, end of the key loop, last epilogue store
  *           issued (0 if the wave stores nothing: a split that does not merge, rows past S,

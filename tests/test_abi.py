@@ -47,7 +47,7 @@ def header_functions():
 
 def test_header_and_library_agree(L):
     names = header_functions()
-    assert len(names) == 26
+    assert len(names) == 27
     for n in names:
         assert hasattr(L, n), n
     assert sorted(_lib.SIGNATURES) == names
@@ -292,10 +292,12 @@ SCHEDULE_SHAPES = [(1, 256, 2, 64), (1, 4608, 3, 128), (1, 4608, 3, 64), (2, 460
 @pytest.mark.parametrize("B,S,H,D", SCHEDULE_SHAPES)
 def test_schedule_partitions_every_tile(L, B, S, H, D):
     """Host-only: every tile's splits cover its key blocks [0, ceil(S/64)) exactly once, in
-    split order, and every workgroup has its own (tile, split)."""
+    split order, and every workgroup has its own (tile, split); tiles are of the launch's
+    rows per workgroup."""
     tile, split, j0, j1 = (np.array(a) for a in xs.xstage_attn_a2a_schedule(B, S, H, D))
     nwg, nsp = xs.xstage_attn_a2a_plan(B, S, H, D)
-    n_tiles, nkv = B * H * ((S + 127) // 128), (S + 63) // 64
+    rows = xs.xstage_attn_a2a_wg_rows(B, S, H, D)
+    n_tiles, nkv = B * H * ((S + rows - 1) // rows), (S + 63) // 64
     assert len(tile) == nwg == n_tiles * nsp
     assert len(set(zip(tile.tolist(), split.tolist()))) == nwg
     for t in range(n_tiles):
@@ -337,6 +339,40 @@ def test_schedule_mixes_placements_in_one_round(L):
     # multi-round launches keep equal ranges (the last split may be shorter)
     tile, split, j0, j1 = (np.array(a) for a in xs.xstage_attn_a2a_schedule(1, 16896, 3, 128))
     assert len(set((j1 - j0)[j1 < (16896 + 63) // 64].tolist())) == 1
+
+
+# (B, S, H, D, split workspace bytes or None for the full plan) -> rows per workgroup, on
+# 256 CUs (the host's default without a device)
+WG_ROWS_CASES = [
+    ((1, 4608, 3, 128, None), 128),   # one round of 432 with placement-sized ranges
+    ((1, 16896, 3, 128, None), 256),  # 1980 4-wave workgroups in ~3.9 rounds -> 990 of 8 waves
+    ((1, 32760, 5, 128, None), 256),  # 2560 -> 1280
+    ((1, 16384, 4, 128, None), 256),  # 512 unsplit (two per CU) -> 256
+    ((1, 16384, 4, 128, 0), 256),     # the same without workspace
+    ((1, 16896, 3, 128, 0), 128),     # 396 unsplit: fewer than two per CU
+    ((1, 9216, 3, 128, None), 128),   # 432 with 2 splits: the one-round table
+    ((1, 12160, 4, 128, None), 128),  # 95 tiles of 128 rows per head (odd)
+    ((1, 16384, 4, 64, None), 256),
+    ((2, 4608, 3, 128, None), 128),   # 432 with 2 splits
+]
+
+
+@pytest.mark.parametrize("shape,rows", WG_ROWS_CASES)
+def test_wg_rows_rule(L, shape, rows):
+    """Host-only: 256-row (8-wave) workgroups exactly where the 4-wave launch keeps every CU at
+    two workgroups without the one-round table and every (b, h) has an even number of 128-row
+    tiles; the workgroup count halves, the split count and workspace bytes stay."""
+    B, S, H, D, wsb = shape
+    assert xs.xstage_attn_a2a_wg_rows(B, S, H, D, wsb) == rows
+    nwg, nsp = xs.xstage_attn_a2a_plan(B, S, H, D, wsb)
+    tiles128 = B * H * ((S + 127) // 128)
+    assert nwg * rows == tiles128 * nsp * 128
+    if nsp > 1:
+        assert xs.xstage_attn_split_ws_size(B, S, H, D) == 16384 + tiles128 * nsp * 4 * (2 * (D // 32) + 1) * 64 * 16
+    n = _lib.ctypes.c_int(0)
+    assert L.xstage_attn_a2a_wg_rows(B, S, H, D, 0, None) == INVALID
+    assert L.xstage_attn_a2a_wg_rows(B, S, H, 80, 0, _lib.ctypes.byref(n)) == UNSUPPORTED
+    assert L.xstage_attn_a2a_wg_rows(0, S, H, D, 0, _lib.ctypes.byref(n)) == INVALID
 
 
 def test_schedule_rejects(L):

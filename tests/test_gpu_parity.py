@@ -344,7 +344,7 @@ def test_bound_launches_equal_direct_calls():
     assert np.array_equal(g3.slabs_host(), ref)
 
 
-@pytest.mark.parametrize("name", ["tiny", "flux1024"])
+@pytest.mark.parametrize("name", ["tiny", "flux1024", "flux2048"])
 def test_traced_modes(name):
     """The instrumented call: modes 0, 1 and 3 write the fused result bit for bit, mode 2
     writes nothing; per-wave stamps are ordered, exactly the waves owning output rows of a
@@ -355,9 +355,12 @@ def test_traced_modes(name):
     q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
     ref = run_fused(w, qb, kb, vb, w.scale).slabs_host()
     nwg, nsp = xs.xstage_attn_a2a_plan(w.B, w.S, w.H, w.D)
+    rows = xs.xstage_attn_a2a_wg_rows(w.B, w.S, w.H, w.D)  # 256 (8 waves) at FLUX-2048
+    waves = rows // 32
+    log(f"[{name}] traced: {nwg} workgroups of {rows} rows, {nsp} key splits")
     for mode in (0, 1, 2):
         g = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
-        stamps = torch.zeros(nwg * 16, dtype=torch.int64, device="cuda")
+        stamps = torch.zeros(nwg * waves * 4, dtype=torch.int64, device="cuda")
         xs.xstage_attn_a2a_fwd_traced(q, k, v, g.views, mode, stamps, w.scale, split_ws=split_ws())
         torch.cuda.synchronize()
         assert g.guards_intact()
@@ -365,12 +368,12 @@ def test_traced_modes(name):
             assert np.all(g.slabs_host() == NAN_BF16)
         else:
             assert np.array_equal(g.slabs_host(), ref), mode
-        st = stamps.cpu().numpy().reshape(nwg, 4, 4)
+        st = stamps.cpu().numpy().reshape(nwg, waves, 4)
         assert np.all(st[:, :, 0] > 0) and np.all(st[:, :, 1] >= st[:, :, 0])
         emit = st[:, :, 2] > 0
         assert np.all(st[emit][:, 2] >= st[emit][:, 1])
         n_tiles = nwg // nsp
-        row_waves = sum(min(4, -(-(w.S - 128 * (t % (n_tiles // (w.B * w.H)))) // 32)) for t in range(n_tiles))
+        row_waves = sum(min(waves, -(-(w.S - rows * (t % (n_tiles // (w.B * w.H)))) // 32)) for t in range(n_tiles))
         assert emit.sum() == (0 if mode == 2 else row_waves), (mode, emit.sum(), row_waves)
         if mode == 1:
             assert np.all(st[emit][:, 3] >= st[emit][:, 2]) and np.all(st[emit][:, 3] > 0)
@@ -378,11 +381,11 @@ def test_traced_modes(name):
             assert np.all(st[:, :, 3] == 0)
     # mode 3: the fused result, and shader-clock ticks at start / loop end in entries 2, 3
     g = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
-    stamps = torch.zeros(nwg * 16, dtype=torch.int64, device="cuda")
+    stamps = torch.zeros(nwg * waves * 4, dtype=torch.int64, device="cuda")
     xs.xstage_attn_a2a_fwd_traced(q, k, v, g.views, 3, stamps, w.scale, split_ws=split_ws())
     torch.cuda.synchronize()
     assert g.guards_intact() and np.array_equal(g.slabs_host(), ref)
-    st = stamps.cpu().numpy().reshape(nwg, 4, 4).astype(np.int64)
+    st = stamps.cpu().numpy().reshape(nwg, waves, 4).astype(np.int64)
     assert np.all(st[:, :, 3] >= st[:, :, 2]) and np.all(st[:, :, 2] > 0)
     long = (st[:, :, 1] - st[:, :, 0]) > 200  # loops of >= 2 us of wall clock
     ghz = (st[:, :, 3] - st[:, :, 2])[long] / ((st[:, :, 1] - st[:, :, 0])[long] / xs.xstage_wallclock_hz()) / 1e9
