@@ -70,3 +70,34 @@ def test_noalloc_matches_workspace_call():
         err = np.abs(o - oracle.attention_fp64(q64, k64, v64, w.scale))
         log(f"no-alloc [{w.name}] max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
         assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, w.name
+
+
+def test_noalloc_eight_wave_launch():
+    """A launch of 256-row (8-wave) workgroups whose key splits merge through the static scratch
+    (B=1, S=12288, H_local=3: 3 splits in a 32 MiB scratch, 432 workgroups in ~1.7 rounds):
+    the bits of the workspace call with a workspace of the scratch's size, and the oracle's
+    values on sampled rows."""
+    w = Workload("noalloc-wide", 1, 12288, 3, 128, 8, seed=53)
+    nwg, nsp = xs.xstage_attn_a2a_plan(w.B, w.S, w.H, w.D, SCRATCH_BYTES)
+    rows = xs.xstage_attn_a2a_wg_rows(w.B, w.S, w.H, w.D, SCRATCH_BYTES)
+    log(f"no-alloc: {w.name} B={w.B} S={w.S} H={w.H} D={w.D} P={w.P}: {nwg} workgroups of {rows} rows, {nsp} key splits")
+    assert rows == 256 and nsp > 1
+    qb, kb, vb = make_inputs(w)
+    q, k, v = (to_dev(x) for x in (qb, kb, vb))
+    ws = torch.zeros(SCRATCH_BYTES, dtype=torch.uint8, device="cuda")
+    ref = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
+    xs.xstage_attn_a2a_fwd(q, k, v, ref.views, w.scale, split_ws=ws)
+    g = GuardedSlabs(w.P, w.B, w.S // w.P, w.H, w.D)
+    xs.xstage_attn_a2a_fwd_noalloc(q, k, v, g.views, w.scale)
+    torch.cuda.synchronize()
+    got = g.slabs_host()
+    assert g.guards_intact() and ref.guards_intact()
+    assert not np.any(got == NAN_BF16)
+    assert np.array_equal(got, ref.slabs_host())
+    rows_s = np.unique(np.concatenate([np.arange(0, w.S, 97), np.arange(w.S - 40, w.S)]))
+    q64, k64, v64 = (oracle.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    o = oracle.ulysses_gather(oracle.bf16_bits_to_f64(got))[:, rows_s]
+    want = oracle.attention_fp64(q64, k64, v64, w.scale, rows=rows_s)
+    err = np.abs(o - want)
+    log(f"no-alloc [{w.name}] sampled rows {len(rows_s)}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
