@@ -249,24 +249,43 @@ __global__ __launch_bounds__(64 * NW, (MODE == kPaced || NW == 8) ? 1 : 2) void 
   const int kv_rows = SRC == kShardQ ? S : a.src_rows;  // rows per K/V buffer
 
   // Q fragment (B operand of the score MFMA): lane holds query (lane & 31), d = 16ks + 8*hl + 0..7
+  const int wave_u32 = __builtin_amdgcn_readfirstlane(w);
   bf16x8 qf[C::KS];
-  {
+  if constexpr (SRC == kPlain) {
     const int qrow = m0 + w * 32 + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < S) {
-        const uint16_t* qb;
-        int r = qrow;
-        if constexpr (SRC != kPlain) {
-          const int p = qrow / a.src_rows;
-          r = qrow - p * a.src_rows;
-          qb = src.q[p] + qhead0;
-        } else {
-          qb = a.q + qhead0;
-        }
-        x = *reinterpret_cast<const u32x4*>(qb + (uint32_t)r * rq + ks * 16 + hl * 8);
-      }
+      if (qrow < S) x = *reinterpret_cast<const u32x4*>(a.q + qhead0 + (uint32_t)qrow * rq + ks * 16 + hl * 8);
+      x ^= a.qflip;
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  } else {
+    // Q from the sequence shards.  The shard pointer is not a per-lane load: when a shard
+    // holds at least 32 rows, a wave's rows lie in at most two shards, whose pointers are
+    // read as wave-uniform scalar values.  The loads are branch-free (a row past S loads row
+    // S - 1 and is zeroed by a select) and global rather than flat accesses, so neither they
+    // nor the pointer fetch are waited on before the first K/V copies are issued.
+    const int qrow = m0 + w * 32 + (lane & 31);
+    const bool q_ok = qrow < S;
+    const int qr = q_ok ? qrow : S - 1;
+    const int p = qr / a.src_rows;
+    const int r = qr - p * a.src_rows;
+    const uint16_t* qb;
+    if (a.src_rows >= 32) {
+      const int p_lo = __builtin_amdgcn_readfirstlane(min(m0 + wave_u32 * 32, S - 1) / a.src_rows);
+      const int p_hi = __builtin_amdgcn_readfirstlane(min(p_lo + 1, S / a.src_rows - 1));
+      const uint16_t* const b_lo = uniform_ptr(src.q[p_lo]);
+      const uint16_t* const b_hi = uniform_ptr(src.q[p_hi]);
+      qb = (p == p_lo ? b_lo : b_hi) + qhead0;
+    } else {
+      qb = src.q[p] + qhead0;
+    }
+    const uint16_t* const qp = qb + (uint32_t)r * rq + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 x = *(const g_u32x4*)(qp + ks * 16);
+      x = q_ok ? x : u32x4{0u, 0u, 0u, 0u};
       x ^= a.qflip;
       qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
