@@ -265,7 +265,8 @@ int xstage_attn_a2a_fwd_traced(const void* q, const void* k, const void* v, void
  * every 128-row tile split into exactly n_split ranges (1: no split) instead of the count the
  * library's model picks; the same decomposition otherwise (ranges sized to the workgroups'
  * CU placement when every workgroup fits on the device at once, equal ranges of 64-key
- * blocks otherwise), and the same result contract: with the model's own count the slabs
+ * blocks otherwise, 256-row workgroups under the same rule as xstage_attn_a2a_wg_rows with
+ * this split count), and the same result contract: with the model's own count the slabs
  * equal xstage_attn_a2a_fwd's bit for bit.
  *   n_split: 1..15, and ceil(S / 64) blocks must form exactly n_split non-empty equal
  *            ranges; shapes with more than 4096 tiles take n_split = 1 only;
