@@ -12,7 +12,8 @@
 // inputs and fp32 accumulation (weights [N, K], K contiguous, as a linear layer stores
 // them): v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand, so a lane holds
 // four consecutive output columns of one token row; operands go global -> LDS with
-// buffer_load_dwordx4 ... lds, double-buffered, XOR-swizzled; the tile is restaged through
+// buffer_load_dwordx4 ... lds, XOR-swizzled, weight blocks two ahead (three slots), token
+// blocks one ahead (two slots); the tile is restaged through
 // LDS so every store is a 16-byte chunk of a 256-byte row segment.  Linear-1 tiles write H
 // (bf16, [tokens, d_ff]); Linear-2 tiles send each token row to (dst_slab[t], dst_row[t]).
 // Linear-2 of an expert reads H written by an earlier launch, so stream order carries the
@@ -43,10 +44,11 @@ constexpr int kMixPerL1 = 1;
 
 __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(const MoeLaunchArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // Weight (A) and token (B) blocks, two slots each, as separate LDS objects (the compiler
-  // then tracks the asynchronous copies per slot).
+  // Weight (A) blocks in three slots, token (B) blocks in two, as separate LDS objects (the
+  // compiler then tracks the asynchronous copies per slot); 80 KiB, two workgroups per CU.
   __shared__ __attribute__((aligned(16))) char lds_w0[kSlot];
   __shared__ __attribute__((aligned(16))) char lds_w1[kSlot];
+  __shared__ __attribute__((aligned(16))) char lds_w2[kSlot];
   __shared__ __attribute__((aligned(16))) char lds_x0[kSlot];
   __shared__ __attribute__((aligned(16))) char lds_x1[kSlot];
 
@@ -101,16 +103,19 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(const MoeLaunchArgs a)
     const int row = c >> 3, lc = (c & 7) ^ ((row >> 1) & 7);
     ld_off[l] = (uint32_t)row * K * 2u + lc * 16u;
   }
-  auto wslot = [&](int s) -> char* { return s ? lds_w1 : lds_w0; };
+  auto wslot = [&](int s) -> char* { return s == 0 ? lds_w0 : s == 1 ? lds_w1 : lds_w2; };
   auto xslot = [&](int s) -> char* { return s ? lds_x1 : lds_x0; };
-  auto load = [&](int s, int kb) {
+  auto load_w = [&](int s, int kb) {
 #pragma unroll
-    for (int l = 0; l < 4; ++l) {
+    for (int l = 0; l < 4; ++l)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(wslot(s) + (l * 4 + wu) * 1024),
                                                16, ld_off[l] + kb * (kTK * 2), 0, 0, 0);
+  };
+  auto load_x = [&](int s, int kb) {
+#pragma unroll
+    for (int l = 0; l < 4; ++l)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(xslot(s) + (l * 4 + wu) * 1024),
                                                16, ld_off[l] + kb * (kTK * 2), 0, 0, 0);
-    }
   };
 
   // Wave w computes output columns wn .. wn+63 (weight rows) of token rows wm .. wm+63.
@@ -125,9 +130,9 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(const MoeLaunchArgs a)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) acc[ii][jj] = f32x16{};
 
-  auto compute = [&](int s) {
-    const char* W = wslot(s);
-    const char* X = xslot(s);
+  auto compute = [&](int sw, int sx) {
+    const char* W = wslot(sw);
+    const char* X = xslot(sx);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 af[2], bf[2];
@@ -142,16 +147,49 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(const MoeLaunchArgs a)
     }
   };
 
+  // Weight blocks (streamed from HBM) run two ahead, token blocks (mostly L2 hits) one ahead.
+  // At the start of block kb the token copy of kb+1 is issued before the weight copy of kb+2;
+  // copies complete in issue order, so the wait at the end of the block can leave the latter
+  // (4 copies per thread) outstanding.  The block ends with a bare s_barrier after that wait:
+  // __syncthreads()'s fence would wait for every outstanding copy into LDS.  Slot reuse: the
+  // copies issued at the start of block kb go to the slots read in block kb - 1, which every
+  // wave has finished (its reads consumed by its MFMAs, lgkmcnt(0), then the barrier).
   const int nkb = K / kTK;
-  load(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  load_x(0, 0);
+  load_w(0, 0);
+  if (1 < nkb) load_w(1, 1);
+  if (1 < nkb) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int s = kb & 1;
-    if (kb + 1 < nkb) load(1 - s, kb + 1);
-    compute(s);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  auto step = [&](int kb, const int SW, const int SX) {
+    // SW = kb % 3, SX = kb % 2 (literals after unrolling)
+    if (kb + 1 < nkb) load_x(1 - SX, kb + 1);
+    if (kb + 2 < nkb) load_w((SW + 2) % 3, kb + 2);
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before the block's reads
+    compute(SW, SX);
+    // own copies of block kb+1 landed (only the 4 of block kb+2 may be outstanding); the
+    // block's LDS reads were consumed by its MFMAs; then a bare barrier (no LDS fence, which
+    // would wait for every outstanding copy)
+    if (kb + 2 < nkb) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  };
+  int kb = 0;
+  for (; kb + 6 <= nkb; kb += 6) {
+    step(kb, 0, 0);
+    step(kb + 1, 1, 1);
+    step(kb + 2, 2, 0);
+    step(kb + 3, 0, 1);
+    step(kb + 4, 1, 0);
+    step(kb + 5, 2, 1);
+  }
+  for (; kb < nkb; ++kb) {
+    const int r = kb % 6;
+    if (r == 0) step(kb, 0, 0);
+    else if (r == 1) step(kb, 1, 1);
+    else if (r == 2) step(kb, 2, 0);
+    else if (r == 3) step(kb, 0, 1);
+    else step(kb, 1, 0);
   }
   unsigned long long t_loop = 0;
   if (a.stamps) t_loop = __builtin_amdgcn_s_memrealtime();
