@@ -822,7 +822,9 @@ struct AttnLaunch {
 
 // Width rule.  Eight waves over 256 query rows share every K/V block copied into LDS (half the
 // copies per query row of four waves over 128 rows), which measured 2-6 % faster per launch
-// on MI355X at the same split ranges, but a CU then holds one workgroup instead of two.  They
+// on MI355X at the same split ranges (the same cycles per launch: the chip holds a higher
+// clock under the lighter copy and L2 traffic), but a CU then holds one workgroup instead of
+// two.  They
 // are used when the 4-wave launch keeps every CU at two workgroups without the one-round unit
 // table (no split and at least two workgroups per CU, or more workgroups than fit at once), and
 // every (b, h) has an even number of 128-row tiles: the 256-row tiles then cover the same rows
