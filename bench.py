@@ -231,11 +231,13 @@ def bench_attention(args, torch, xs):
         settle_n += 50
         torch.cuda.synchronize()
 
-    # the timed region: exactly `steps` fused steps bracketed by synchronizations
+    # the timed region: exactly `steps` fused steps bracketed by synchronizations (the events
+    # exist beforehand, so that the GPU idles as briefly as possible between the synchronize
+    # and the first timed launch)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
         fused()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record()
     for _ in range(args.steps):
