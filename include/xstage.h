@@ -28,7 +28,8 @@
  *     into the kernel arguments, so the array may be freed as soon as the call returns.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work and return;
  *     they never synchronize, never allocate and never free memory: the caller owns every
- *     buffer.
+ *     buffer.  A call on a capturing stream is recorded as kernel nodes only (no memset
+ *     nodes) and may be replayed from the graph.
  *   - Split workspace (attention entry points: split_ws, split_ws_bytes).  When a shape has
  *     few 128-row query tiles for the device (small B*H_local*S), the keys of each tile are
  *     split over several workgroups whose partial results meet in a caller-owned workspace:
