@@ -213,9 +213,10 @@ int xstage_attn_a2a_plan(int B, int S, int H_local, int D, unsigned long long sp
 /* Query rows per workgroup of that launch (*rows): 128 (4 waves of 32 rows) or 256 (8 waves;
  * every K/V block staged in LDS then serves twice the rows).  256 is used when the launch with
  * 128 gives every CU two workgroups without placement-sized key ranges (no split and at least
- * two workgroups per CU, or more workgroups than fit at once) and every (b, h) has an even
- * number of 128-row tiles; the key ranges and merge order per query row are then the same,
- * and so is the result, bit for bit.  Plumbing of this work decomposition (the pages fix no
+ * two workgroups per CU, or more workgroups than fit at once), the most 128-row workgroups
+ * any CU runs (ceil(workgroups / CUs)) is even, every key range spans at least 20 64-key
+ * blocks, and every (b, h) has an even number of 128-row tiles; the key ranges and merge
+ * order per query row are then the same, and so is the result, bit for bit.  Plumbing of this work decomposition (the pages fix no
  * tile shape; "Contributions", FlashAttention-A2A item, defines the fused call).  Host only. */
 int xstage_attn_a2a_wg_rows(int B, int S, int H_local, int D, unsigned long long split_ws_bytes,
                             int* rows);

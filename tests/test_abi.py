@@ -354,14 +354,21 @@ WG_ROWS_CASES = [
     ((1, 12160, 4, 128, None), 128),  # 95 tiles of 128 rows per head (odd)
     ((1, 16384, 4, 64, None), 256),
     ((2, 4608, 3, 128, None), 128),   # 432 with 2 splits
+    ((2, 4864, 8, 128, None), 128),   # 1216 with 2 splits: at most 5 per CU (odd)
+    ((4, 6144, 1, 128, None), 128),   # 768 with 4 splits: at most 3 per CU (odd)
+    ((2, 5632, 2, 128, None), 128),   # 880 with 5 splits of 18 64-key blocks (short)
+    ((4, 1792, 5, 128, None), 128),   # 840 with 3 splits of 10 blocks (short)
+    ((4, 6400, 1, 128, None), 256),   # 1000 with 5 splits of 20 blocks: at most 4 per CU
+    ((2, 8448, 2, 128, None), 256),   # 792 with 3 splits of 44 blocks
 ]
 
 
 @pytest.mark.parametrize("shape,rows", WG_ROWS_CASES)
 def test_wg_rows_rule(L, shape, rows):
     """Host-only: 256-row (8-wave) workgroups exactly where the 4-wave launch keeps every CU at
-    two workgroups without the one-round table and every (b, h) has an even number of 128-row
-    tiles; the workgroup count halves, the split count and workspace bytes stay."""
+    two workgroups without the one-round table, the most 4-wave workgroups any CU runs is even,
+    every key range spans at least 20 64-key blocks and every (b, h) has an even number of
+    128-row tiles; the workgroup count halves, the split count and workspace bytes stay."""
     B, S, H, D, wsb = shape
     assert xs.xstage_attn_a2a_wg_rows(B, S, H, D, wsb) == rows
     nwg, nsp = xs.xstage_attn_a2a_plan(B, S, H, D, wsb)
