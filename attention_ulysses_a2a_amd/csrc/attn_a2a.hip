@@ -585,11 +585,16 @@ __global__ __launch_bounds__(64 * NW, (MODE == kPaced || NW == 8) ? 1 : 2) void 
   // merges them (rescaling by exp2(m_s - m)) and runs the epilogue for the tile.
   if (!kPace && a.n_split > 1) {
     __shared__ int last_flag;
-    // One record per (tile, split, wave), in lane-major 16-byte chunks: the unnormalised O
-    // rounded to bf16 (two chunks per 32-wide d tile, accumulator registers 0..7 and 8..15),
-    // then (m, l) in fp32.  bf16 halves the bytes written here and read back by the merge,
-    // both of which sit on the tail of the kernel; the rounding adds at most one bf16 unit
-    // in the last place relative to each partial, inside the output's own rounding scale.
+    // One record per (tile, split, wave), in lane-major 16-byte chunks: the lane's
+    // unnormalised O rounded to fp16 (two chunks per 32-wide d tile, accumulator registers
+    // 0..7 and 8..15), then (m, l, 2^E) in fp32.  16-bit values halve the bytes written here
+    // and read back by the merge, both of which sit on the tail of the kernel; fp16's 11-bit
+    // significand keeps each partial within 2^-11 of itself (bf16 would allow 2^-8 + 2^-9 per
+    // output, more than a 1e-2 bound leaves beside the output's own bf16 rounding once |O|
+    // reaches 2).  A lane whose largest |O| reaches 2^15 stores O * 2^-E instead, E >= 1
+    // chosen so that the values stay below 2^15 (fp16 overflows at 65520); otherwise E = 0.
+    // Values that fall below fp16's normal range lose at most 2^-25 absolutely, and the merged
+    // sum of weights L is at least 1, so the output loses no more.
     constexpr int OCH = 2 * C::DT;
     constexpr int PREC = OCH + 1;
     // The workspace is ordinary device memory, cached in each XCD's own L2, and the splits of a
@@ -602,22 +607,38 @@ __global__ __launch_bounds__(64 * NW, (MODE == kPaced || NW == 8) ? 1 : 2) void 
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(a.partial, (short)0, a.partial_bytes, 0x00020000);
     auto rec = [&](int sp) { return (((uint32_t)(tile * a.n_split + sp) * (uint32_t)NW + (uint32_t)w) * PREC * 64u + (uint32_t)lane) * 16u; };
     u32x4 own[OCH];  // this split's record, kept for the merge should it arrive last
+    float own_unscale;
     {
+      float mx = 0.f;  // largest |O| of the lane (NaN ignored)
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, __builtin_fabsf(o[dt][e]));
+      // E = exponent of mx beyond 2^15 (mx < 2^(15 + E)); an infinite mx takes the largest
+      // finite one's E, so that the finite values beside it keep their place
+      int ex = (mx == __builtin_inff() ? 128 : __builtin_amdgcn_frexp_expf(mx)) - 15;
+      ex = ex < 0 ? 0 : ex;
+      own_unscale = __builtin_ldexpf(1.0f, ex);
       const uint32_t r = rec(split);
+      const bool scaled = __builtin_amdgcn_ballot_w64(ex > 0) != 0;  // wave-uniform
+      const float sc = __builtin_ldexpf(1.0f, -ex);
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const f32x16& x = o[dt];
           const int e0 = 8 * hh;
-          own[2 * dt + hh] = u32x4{pack_bf16x2(x[e0 + 0], x[e0 + 1]), pack_bf16x2(x[e0 + 2], x[e0 + 3]),
-                                   pack_bf16x2(x[e0 + 4], x[e0 + 5]), pack_bf16x2(x[e0 + 6], x[e0 + 7])};
+          own[2 * dt + hh] =
+              scaled ? u32x4{pack_f16x2(x[e0 + 0] * sc, x[e0 + 1] * sc), pack_f16x2(x[e0 + 2] * sc, x[e0 + 3] * sc),
+                             pack_f16x2(x[e0 + 4] * sc, x[e0 + 5] * sc), pack_f16x2(x[e0 + 6] * sc, x[e0 + 7] * sc)}
+                     : u32x4{pack_f16x2(x[e0 + 0], x[e0 + 1]), pack_f16x2(x[e0 + 2], x[e0 + 3]),
+                             pack_f16x2(x[e0 + 4], x[e0 + 5]), pack_f16x2(x[e0 + 6], x[e0 + 7])};
           __builtin_amdgcn_raw_buffer_store_b128(own[2 * dt + hh], prs, r + (2 * dt + hh) * 1024u, 0, kDeviceScope);
         }
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m_run, l_run, 0.f, 0.f}), prs,
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m_run, l_run, own_unscale, 0.f}), prs,
                                              r + OCH * 1024u, 0, kDeviceScope);
     }
-    const f32x4 own_ml = {m_run, l_run, 0.f, 0.f};
+    const f32x4 own_ml = {m_run, l_run, own_unscale, 0.f};
     // Wait until this wave's record stores have completed (device-scope stores complete once
     // they reach the coherence point); the barrier then orders all four waves' records before
     // the arrival count, an agent-scope atomic performed at the coherence point.
@@ -672,15 +693,19 @@ __global__ __launch_bounds__(64 * NW, (MODE == kPaced || NW == 8) ? 1 : 2) void 
       for (int i = 0; i < NB; ++i) {
         const float f = __builtin_amdgcn_exp2f(ml[i][0] - m_new);
         l_acc += ml[i][1] * f;
+        const float fs = f * ml[i][2];  // the record holds O * 2^-E; ml[i][2] = 2^E (1 unless scaled)
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
+              // copied to a scalar first: this compiler reads element 0 for a bit cast applied
+              // to a vector element directly, whatever the index
               const uint32_t wv = ob[i][2 * dt + hh][k];
-              o[dt][8 * hh + 2 * k] += __uint_as_float(wv << 16) * f;
-              o[dt][8 * hh + 2 * k + 1] += __uint_as_float(wv & 0xffff0000u) * f;
+              const f16x2 hv = __builtin_bit_cast(f16x2, wv);
+              o[dt][8 * hh + 2 * k] += (float)hv[0] * fs;
+              o[dt][8 * hh + 2 * k + 1] += (float)hv[1] * fs;
             }
       }
       m_acc = m_new;

@@ -27,8 +27,8 @@ struct SplitPlan {
 // this; a launch given less workspace splits less).
 constexpr size_t kSplitPartialCap = size_t(128) << 20;
 
-// Bytes of split partials of one (tile, split) unit: 4 waves x (2 bf16 O chunks per 32-wide
-// d tile + one (m, l) chunk) x 64 lanes x 16 B.
+// Bytes of split partials of one (tile, split) unit: 4 waves x (2 fp16 O chunks per 32-wide
+// d tile + one (m, l, scale) chunk) x 64 lanes x 16 B.
 inline size_t partial_bytes_per_unit(int D) { return (size_t)4 * (2 * (D / 32) + 1) * 64 * 16; }
 
 // Workspace layout, the same for every shape: kSplitMaxTiles uint32 arrival counters (tile t

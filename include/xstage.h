@@ -47,8 +47,11 @@
  *     launched and no output byte is touched.  Faults inside kernels surface at the
  *     caller's next synchronization.  XSTAGE_ERR_HIP reports the HIP launch status.
  *   - Attention: O = softmax(scale * Q K^T) V per (b, h), non-causal, products and sums in
- *     fp32, output rounded to bf16 (round to nearest, ties to even).  scale may be any
- *     finite value, including 0 and negative values.
+ *     fp32, output rounded to bf16 (round to nearest, ties to even).  When a tile's keys are
+ *     split over workgroups, each split's partial sums pass through an fp16 record (within
+ *     2^-11 of themselves; scaled by a power of two where they would exceed fp16's range)
+ *     before they are merged in fp32.  scale may be any finite value, including 0 and
+ *     negative values.
  *   - Thread safety: the library keeps no device state; its host-side caches (CU count and
  *     per-shape schedule tables) are guarded by a mutex; entry points may be called
  *     concurrently.
