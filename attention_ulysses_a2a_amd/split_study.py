@@ -2,8 +2,8 @@
 
 The fused kernel splits the key range of each 128-row tile into n_split ranges when the
 shape has too few tiles to fill the device, merging the partial softmax states through the
-caller's workspace; the count comes from a cost model fitted on MI355X at H_local = 3,
-D = 128 (``choose_split`` in csrc/workspace.hip).  This times every available count on
+caller's workspace; the count comes from a cost model fitted on MI355X measurements
+(``choose_split`` in csrc/workspace.hip).  This times every available count on
 each shape with ``xstage_attn_a2a_fwd_nsplit`` (HIP events on the current stream, inputs
 resident, after a settle phase; three interleaved rounds, medians) and reports the model's
 count, the fastest measured count and what the model's count loses against it.
@@ -34,82 +34,121 @@ def _time(torch, fn, n, warm):
     return s.elapsed_time(e) / n * 1e-3
 
 
-def run(torch, xs, S_list=DEFAULT_S, H_list=DEFAULT_H, D_list=DEFAULT_D, rounds=3, target_s=0.03, settle_s=0.3,
-        emit=print):
-    from synth import Workload, make_inputs
+def grid_shapes(S_list=DEFAULT_S, H_list=DEFAULT_H, D_list=DEFAULT_D):
+    """The fixed grid: B = 1, every (S, H_local, D) of the three lists."""
+    return [(1, S, H, D) for D in D_list for H in H_list for S in S_list]
 
-    ws = torch.zeros((129 << 20,), dtype=torch.uint8, device="cuda")
-    out, settled = [], False
-    for D in D_list:
-        for H in H_list:
-            for S in S_list:
-                w = Workload("split", 1, S, H, D, 8, seed=S + 7 * H + D)
-                qb, kb, vb = make_inputs(w)
-                q, k, v = (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
-                           for x in (qb, kb, vb))
-                slabs = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device="cuda")
-                counts = []
-                for n in range(1, MAX_SPLIT + 1):
-                    try:
-                        need = xs.xstage_attn_nsplit_ws_size(1, S, H, D, n)
-                    except xs.XStageError:
-                        continue
-                    if need <= ws.numel():
-                        counts.append(n)
-                legs = {n: xs.bind("xstage_attn_a2a_fwd_nsplit", q, k, v, slabs, n, w.scale,
-                                   split_ws=ws if n > 1 else None) for n in counts}
-                model_n = xs.xstage_attn_a2a_plan(1, S, H, D)[1]
-                if not settled:  # the chip's clock ramps over the first launches of a process
-                    fn = legs[model_n]
-                    t1 = _time(torch, fn, 3, 1)
-                    _time(torch, fn, max(1, int(settle_s / max(t1, 1e-6))), 0)
-                    settled = True
-                per = {n: [] for n in counts}
-                for _ in range(rounds):
-                    for n, fn in legs.items():
-                        t = _time(torch, fn, 2, 1)
-                        per[n].append(_time(torch, fn, max(3, int(target_s / max(t, 1e-6))), 2))
-                us = {n: float(np.median(v)) * 1e6 for n, v in per.items()}
-                best = min(us, key=us.get)
-                line = {"split_study": f"S={S} H={H} D={D}", "S": S, "H": H, "D": D,
-                        "n_tiles": H * ((S + 127) // 128), "us": {str(n): round(t, 3) for n, t in us.items()},
-                        "model_split": model_n, "best_split": best,
-                        "model_loss_pct": (us[model_n] / us[best] - 1) * 100}
-                emit(json.dumps(line))
-                out.append(line)
-                del legs, q, k, v, slabs
+
+def random_shapes(seed: int, n: int):
+    """A seeded draw of n shapes in the range where key splits matter: B in {1, 2, 4},
+    H_local 1-8, D 64 or 128, S a multiple of 8 in [512, 20000), kept when the shape has
+    8-1200 tiles of 128 query rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B = int(rng.choice([1, 2, 4]))
+        H = int(rng.integers(1, 9))
+        D = int(rng.choice([64, 128]))
+        S = int(rng.integers(64, 2500)) * 8
+        if 8 <= B * H * ((S + 127) // 128) <= 1200:
+            out.append((B, S, H, D))
     return out
 
 
-def summarize(lines, command: str, source_hash: str) -> str:
+def run(torch, xs, shapes=None, label="grid", rounds=3, target_s=0.03, settle_s=0.3, emit=print):
+    from synth import Workload, make_inputs
+
+    shapes = grid_shapes() if shapes is None else shapes
+    ws = torch.zeros((129 << 20,), dtype=torch.uint8, device="cuda")
+    out, settled = [], False
+    for B, S, H, D in shapes:
+        w = Workload("split", B, S, H, D, 8, seed=S + 7 * H + D + B - 1)
+        qb, kb, vb = make_inputs(w)
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+                   for x in (qb, kb, vb))
+        slabs = torch.empty((w.P, w.B, w.S // w.P, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+        counts = []
+        for n in range(1, MAX_SPLIT + 1):
+            try:
+                need = xs.xstage_attn_nsplit_ws_size(B, S, H, D, n)
+            except xs.XStageError:
+                continue
+            if need <= ws.numel():
+                counts.append(n)
+        legs = {n: xs.bind("xstage_attn_a2a_fwd_nsplit", q, k, v, slabs, n, w.scale,
+                           split_ws=ws if n > 1 else None) for n in counts}
+        model_n = xs.xstage_attn_a2a_plan(B, S, H, D)[1]
+        if not settled:  # the chip's clock ramps over the first launches of a process
+            fn = legs[model_n]
+            t1 = _time(torch, fn, 3, 1)
+            _time(torch, fn, max(1, int(settle_s / max(t1, 1e-6))), 0)
+            settled = True
+        per = {n: [] for n in counts}
+        for _ in range(rounds):
+            for n, fn in legs.items():
+                t = _time(torch, fn, 2, 1)
+                per[n].append(_time(torch, fn, max(3, int(target_s / max(t, 1e-6))), 2))
+        us = {n: float(np.median(v)) * 1e6 for n, v in per.items()}
+        best = min(us, key=us.get)
+        line = {"split_study": f"B={B} S={S} H={H} D={D}", "set": label, "B": B, "S": S, "H": H, "D": D,
+                "n_tiles": B * H * ((S + 127) // 128), "us": {str(n): round(t, 3) for n, t in us.items()},
+                "model_split": model_n, "best_split": best,
+                "model_loss_pct": (us[model_n] / us[best] - 1) * 100}
+        emit(json.dumps(line))
+        out.append(line)
+        del legs, q, k, v, slabs
+    return out
+
+
+def _stats(lines) -> str:
     losses = np.array([ln["model_loss_pct"] for ln in lines])
+    return (f"over {len(lines)} shapes the model's count is the fastest measured on "
+            f"{int(np.sum(losses <= 0.0))}, within 2 % on {int(np.sum(losses <= 2.0))} and within 5 % on "
+            f"{int(np.sum(losses <= 5.0))}; mean loss {losses.mean():.2f} %, largest {losses.max():.2f} %")
+
+
+def summarize(lines, commands, source_hash: str) -> str:
+    commands = [commands] if isinstance(commands, str) else list(commands)
+    sets = []
+    for ln in lines:
+        if ln.get("set", "grid") not in sets:
+            sets.append(ln.get("set", "grid"))
     md = ["# Key-split count: the model's choice against every count measured (one MI355X)", "",
-          "Command (repository root):", "", f"    {command}", "",
+          "Commands (repository root):", ""] + [f"    {c}" for c in commands] + ["",
           f"Kernel source hash (attn_a2a.hip + common.hpp, sha256 prefix): `{source_hash}`.", "",
-          "B = 1, P = 8, seeded N(0,1) inputs resident in HBM; every available split count 1.."
+          "P = 8, seeded N(0,1) inputs resident in HBM; every available split count 1.."
           f"{MAX_SPLIT} timed with `xstage_attn_a2a_fwd_nsplit` (HIP events, back-to-back launches, three "
           "interleaved rounds after a settle phase, medians).  'model' is the count the product call "
-          "(`xstage_attn_a2a_fwd` with a full workspace) uses.", "",
-          f"Over {len(lines)} shapes the model's count is the fastest measured on "
-          f"{int(np.sum(losses <= 0.0))}, within 2 % on {int(np.sum(losses <= 2.0))} and within 5 % on "
-          f"{int(np.sum(losses <= 5.0))}; median loss {np.median(losses):.2f} %, largest {losses.max():.2f} %.", "",
-          "| S | H | D | tiles | model n_split | µs | fastest n_split | µs | model loss |",
-          "|---|---|---|---|---|---|---|---|---|"]
+          "(`xstage_attn_a2a_fwd` with a full workspace) uses.", ""]
+    for name in sets:
+        sel = [ln for ln in lines if ln.get("set", "grid") == name]
+        md.append(f"* {name}: {_stats(sel)}.")
+    if len(sets) > 1:
+        md.append(f"* all: {_stats(lines)}.")
+    md += ["", "| set | B | S | H | D | tiles | model n_split | µs | fastest n_split | µs | model loss |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
     for ln in lines:
         us = {int(k): v for k, v in ln["us"].items()}
-        md.append(f"| {ln['S']} | {ln['H']} | {ln['D']} | {ln['n_tiles']} | {ln['model_split']} | "
-                  f"{us[ln['model_split']]:.1f} | {ln['best_split']} | {us[ln['best_split']]:.1f} | "
+        md.append(f"| {ln.get('set', 'grid')} | {ln.get('B', 1)} | {ln['S']} | {ln['H']} | {ln['D']} | {ln['n_tiles']} | "
+                  f"{ln['model_split']} | {us[ln['model_split']]:.1f} | {ln['best_split']} | {us[ln['best_split']]:.1f} | "
                   f"{ln['model_loss_pct']:+.2f} % |")
     md += ["", "Time of every count (µs):", ""]
     for ln in lines:
-        md.append(f"* S={ln['S']} H={ln['H']} D={ln['D']}: "
+        md.append(f"* B={ln.get('B', 1)} S={ln['S']} H={ln['H']} D={ln['D']}: "
                   + ", ".join(f"{k}: {v:.1f}" for k, v in ln["us"].items()))
     return "\n".join(md) + "\n"
 
 
-if __name__ == "__main__":  # python -m attention_ulysses_a2a_amd.split_study <jsonl> <source hash> [command]
+if __name__ == "__main__":  # python -m attention_ulysses_a2a_amd.split_study <source hash> <jsonl> [<jsonl> ...]
     import sys
 
-    lines = [json.loads(x) for x in open(sys.argv[1]) if x.startswith("{\"split_study\"")]
-    cmd = sys.argv[3] if len(sys.argv) > 3 else "python bench.py --split-study"
-    print(summarize(lines, cmd, sys.argv[2]), end="")
+    lines = [json.loads(x) for f in sys.argv[2:] for x in open(f) if x.startswith("{\"split_study\"")]
+    cmds = ["python bench.py --split-study > gpurun_out/split_study.jsonl"]
+    for name in dict.fromkeys(ln.get("set", "grid") for ln in lines):
+        if name.startswith("random seed "):  # "random seed <seed>, <n> shapes"
+            seed, n = name[len("random seed "):].split(", ")
+            cmds.append(f"python bench.py --split-study --split-random {seed} {n.split()[0]} "
+                        f"> gpurun_out/split_random_{seed}.jsonl")
+    cmds.append("python -m attention_ulysses_a2a_amd.split_study <hash> gpurun_out/split_study.jsonl "
+                "gpurun_out/split_random_*.jsonl")
+    print(summarize(lines, cmds, sys.argv[1]), end="")

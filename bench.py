@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--split-study", action="store_true",
                     help="every key-split count against the split-count model over a grid of shapes "
                          "(one JSON line per shape)")
+    ap.add_argument("--split-random", nargs=2, type=int, metavar=("SEED", "N"), default=None,
+                    help="with --split-study: N shapes of a seeded random draw instead of the grid")
     ap.add_argument("--paced", action="store_true",
                     help="paced persistent epilogue: every chunk count against the product call and the "
                          "Burst-Gap model's choice (one JSON line per workload)")
@@ -445,9 +447,14 @@ def main():
         run_study(torch, xs, emit=lambda line: print(line, flush=True))
         return
     if args.split_study:
-        from attention_ulysses_a2a_amd.split_study import run as run_split
+        from attention_ulysses_a2a_amd.split_study import random_shapes, run as run_split
 
-        run_split(torch, xs, settle_s=args.settle_s, emit=lambda line: print(line, flush=True))
+        if args.split_random:
+            seed, n = args.split_random
+            run_split(torch, xs, shapes=random_shapes(seed, n), label=f"random seed {seed}, {n} shapes",
+                      settle_s=args.settle_s, emit=lambda line: print(line, flush=True))
+        else:
+            run_split(torch, xs, settle_s=args.settle_s, emit=lambda line: print(line, flush=True))
         return
     if args.paced:
         from attention_ulysses_a2a_amd.paced_study import run as run_paced
