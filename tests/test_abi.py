@@ -203,7 +203,7 @@ def test_fused_rejects_bad_split_workspace(L):
 
 def test_split_ws_size_and_plan(L):
     """The workspace query reports the fastest plan's bytes (counters padded to 256, then the
-    bf16 partial records of every (tile, split) unit); a smaller workspace limits the split
+    16-bit partial records of every (tile, split) unit); a smaller workspace limits the split
     count to what fits, none gives no split."""
     B, S, H, D = 1, 4608, 3, 128
     n_tiles = B * H * ((S + 127) // 128)
