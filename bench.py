@@ -307,6 +307,27 @@ def bench_attention(args, torch, xs):
     use = wall > 2e-6
     loop_ghz = float(np.median(ticks[use] / wall[use]) / 1e9) if use.any() else None
 
+    # Checks of the timed path's own output, outside the timed region and without any
+    # reference implementation: the fused and the serial call write the same slabs bit for
+    # bit, and on the placement probe (inputs whose exact attention output is V itself) the
+    # fused call puts row s of V into slab s // (S/P), row s % (S/P), every element exact.
+    from synth import make_placement_probe
+
+    fused()
+    torch.cuda.synchronize()
+    slabs_fused = slabs.clone()
+    unfused()
+    torch.cuda.synchronize()
+    fused_equals_serial = bool(torch.equal(slabs_fused.view(torch.int16), slabs.view(torch.int16)))
+    probe_scale = 1.0 / math.sqrt(w.D)
+    pq, pk, pv = (dev(x) for x in make_placement_probe(w.B, w.S, w.H, w.D, probe_scale))
+    xs.xstage_attn_a2a_fwd(pq, pk, pv, slab_list, probe_scale, split_ws=sws)
+    torch.cuda.synchronize()
+    expect = pv.view(w.B, w.P, w.S // w.P, w.H, w.D).transpose(0, 1).contiguous()
+    placement_exact = bool(torch.equal(slabs.view(torch.int16), expect.view(torch.int16)))
+    del slabs_fused, pq, pk, pv, expect
+    props = torch.cuda.get_device_properties(0)
+
     tflops = w.flops / (ms * 1e-3) / 1e12
     res = {
         "metric": METRIC if w.S == 4608 else METRIC.replace("(S=4608,", f"(S={w.S},"),
@@ -351,6 +372,10 @@ def bench_attention(args, torch, xs):
         "ms_ulysses_layer_kv_staged": ms_layer_staged,
         "ulysses_kv_staged_vs_in_place": round(ms_layer / ms_layer_staged, 4),
         "wall_s_timed_region": t_wall,
+        "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                "compute_units": props.multi_processor_count},
+        "fused_equals_serial": fused_equals_serial,
+        "placement_probe_exact": placement_exact,
         "loop_clock_ghz": None if loop_ghz is None else round(loop_ghz, 3),
         "pct_of_peak_at_loop_clock": None if loop_ghz is None else
         round(100.0 * tflops / (PEAK_BF16_TFLOPS * loop_ghz / PEAK_CLOCK_GHZ), 2),
