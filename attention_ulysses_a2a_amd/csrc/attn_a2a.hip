@@ -845,31 +845,6 @@ struct AttnLaunch {
   size_t used = 0;  // split workspace bytes the plan uses
 };
 
-// Width rule.  Eight waves over 256 query rows share every K/V block copied into LDS (half the
-// copies per query row of four waves over 128 rows), which measured 2-7 % faster per launch
-// on MI355X at the same split ranges (the same cycles per launch: the chip holds a higher
-// clock under the lighter copy and L2 traffic), but a CU then holds one workgroup instead of
-// two.  That costs in two places, both measured on MI355X (64 shapes, B 1-4, S 1536-32768,
-// H_local 1-8, D 128, four against eight waves at the same split ranges):
-//  - the launch tail: with four waves, a CU left with an odd number of workgroups runs the
-//    last one alone, faster than a pair; eight waves have no such half step and lost 1-12 %
-//    whenever the most 128-row workgroups any CU runs, ceil(units / CUs), was odd;
-//  - short key ranges: nothing overlaps a lone workgroup's prologue (Q load, first K/V
-//    copies) and merge; with fewer than 20 64-key blocks per range that outweighed the
-//    clock gain (0-7 % slower).
-// Eight waves are used when the 4-wave launch keeps every CU at two workgroups without the
-// one-round unit table (no split and at least two workgroups per CU, or more workgroups than
-// fit at once), that per-CU count is even, every key range spans at least 20 blocks, and
-// every (b, h) has an even number of 128-row tiles: the 256-row tiles then cover the same
-// rows with the same key ranges and merge order (results bit for bit those of 4 waves) and
-// the split records take the same workspace bytes.
-static bool wide_launch(int S, int n_tiles4, const SplitPlan& plan, int cus) {
-  const long units4 = (long)n_tiles4 * plan.n_split;
-  const long per_cu = (units4 + cus - 1) / cus;
-  return ((S + 127) / 128) % 2 == 0 && units4 >= 2L * cus && (plan.n_split == 1 || units4 > 2L * cus) &&
-         per_cu % 2 == 0 && plan.kvb_per_split >= 20;
-}
-
 // force_split > 0: exactly that many splits (false if impossible or the workspace is too
 // small); otherwise the model's plan for ws_bytes of workspace.
 static bool attn_launch(int B, int S, int H, int D, unsigned long long ws_bytes, int force_split, bool allow_wide,
@@ -882,7 +857,11 @@ static bool attn_launch(int B, int S, int H, int D, unsigned long long ws_bytes,
   } else {
     L->plan = plan_with_workspace(n_tiles4, nkv, D, ws_bytes, &L->used);
   }
-  L->nw = allow_wide && wide_launch(S, n_tiles4, L->plan, cu_count()) ? 8 : 4;
+  // width rule (workspace.hip, beside the split cost model that prices it)
+  L->nw = allow_wide && wide_rule(((S + 127) / 128) % 2 == 0, (long)n_tiles4 * L->plan.n_split, L->plan.n_split,
+                                  L->plan.kvb_per_split, cu_count())
+              ? 8
+              : 4;
   L->n_tiles = L->nw == 8 ? n_tiles4 / 2 : n_tiles4;
   L->n_units = L->n_tiles * L->plan.n_split;
   return true;

@@ -38,6 +38,12 @@ inline size_t partial_bytes_per_unit(int D) { return (size_t)4 * (2 * (D / 32) +
 constexpr int kSplitMaxTiles = 4096;
 constexpr size_t kCounterAreaBytes = (size_t)kSplitMaxTiles * 4;
 
+// Width rule of an attention launch: true when it runs 8-wave workgroups over 256 query rows
+// instead of 4-wave ones over 128.  even_tiles: every (b, h) has an even number of 128-row
+// tiles; units4: 128-row tiles x key splits; kvb: 64-key blocks per key range; cus: compute
+// units of the device.
+bool wide_rule(bool even_tiles, long units4, int n_split, int kvb, int cus);
+
 // Picks the key-split count of `n_tiles` tiles of 128 query rows over `nkv` blocks of 64
 // keys (head dimension D) on the current device, from a cost model of rounds of
 // co-resident workgroups (two per compute unit) and of the merge of split tiles, among the

@@ -355,7 +355,7 @@ WG_ROWS_CASES = [
     ((1, 16384, 4, 64, None), 256),
     ((2, 4608, 3, 128, None), 128),   # 432 with 2 splits
     ((2, 4864, 8, 128, None), 128),   # 1216 with 2 splits: at most 5 per CU (odd)
-    ((4, 6144, 1, 128, None), 128),   # 768 with 4 splits: at most 3 per CU (odd)
+    ((1, 10496, 5, 128, None), 128),  # 1230 with 3 splits of 55 blocks: at most 5 per CU (odd)
     ((2, 5632, 2, 128, None), 128),   # 880 with 5 splits of 18 64-key blocks (short)
     ((4, 1792, 5, 128, None), 128),   # 840 with 3 splits of 10 blocks (short)
     ((4, 6400, 1, 128, None), 256),   # 1000 with 5 splits of 20 blocks: at most 4 per CU
