@@ -382,6 +382,27 @@ def test_wg_rows_rule(L, shape, rows):
     assert L.xstage_attn_a2a_wg_rows(0, S, H, D, 0, _lib.ctypes.byref(n)) == INVALID
 
 
+NAMED_PLANS = {
+    # workload: (workgroups, key splits, query rows per workgroup) with the full workspace
+    "tiny": (4, 1, 128),
+    "flux1024": (432, 4, 128),
+    "flux2048": (990, 5, 256),
+    "video": (1280, 2, 256),
+}
+
+
+@pytest.mark.parametrize("name", sorted(NAMED_PLANS))
+def test_named_workload_plans(name):
+    """Host-only: the plans the committed kernel traces, counter summaries and traffic figure
+    were measured on.  A change of the split model or the width rule that moves one of them
+    also changes what those measurements describe, so it has to be re-measured with them."""
+    from synth import workload
+
+    w = workload(name)
+    nwg, nsp = xs.xstage_attn_a2a_plan(w.B, w.S, w.H, w.D)
+    assert (nwg, nsp, xs.xstage_attn_a2a_wg_rows(w.B, w.S, w.H, w.D)) == NAMED_PLANS[name]
+
+
 def test_schedule_rejects(L):
     n = _lib.ctypes.c_int(0)
     buf = (_lib.ctypes.c_int * 4)()
